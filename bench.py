@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Throughput of strict selected-token logprob + entropy on one MI355X.
+
+Headline workload: the logits path on Qwen3-vocabulary data -- T = 1024 rows of
+V = 151936 fp32 logits ~ N(0, 3^2) with 1% of rows spiked (+25 at one column), targets
+drawn from softmax(X); one step = one rlk_logprob_from_logits call (logprob + entropy,
+vocab split 1).  Inputs are resident in HBM before timing starts.
+
+Also reported on the same JSON line:
+  roofline      HBM roofline of the row-reduce kernel: algorithmic bytes per launch
+                (1024 x 607760 B: every logit once, the target id, two fp32 outputs)
+                over its mean launch time (HIP events on the launch stream), vs 8 TB/s;
+  cpu_baseline  the float64 CPU oracle on the same rows;
+  fused         the fused linear-logp path on the Qwen3-8B shape (T = 2048, d = 4096,
+                V = 151936 bf16) as tokens/s and fraction of the 2.5 PFLOP/s bf16
+                MFMA peak (2 T V d flops per call);
+  splits        ms per call of the logits path at vocab splits 2, 4, 8.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-fused]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s selected-logprob+entropy at V=151936; % HBM BW / % MFMA peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+BYTES_PER_TOKEN_LOGITS = 151936 * 4 + 8 + 8
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_reduce_T1024_V151936_traffic.json")
+TRAFFIC_SOURCES = ["entropy_rlk_logprob_amd/csrc/rlk_logits.hip",
+                   "entropy_rlk_logprob_amd/csrc/rlk_state.hpp"]
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def sources_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when
+    there is none or the kernel source changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != sources_hash(TRAFFIC_SOURCES):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_calls(fn, steps: int, warmup: int):
+    """Mean ms per call over `steps` calls, each bracketed by HIP events recorded on the
+    current stream (the stream the library launches on); also the total wall ms."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return sum(per) / len(per), wall_ms / steps, per
+
+
+def cpu_baseline(case):
+    import oracle
+    t0 = time.perf_counter()
+    oracle.logprob_entropy(case.x, case.targets, case.temperature)
+    dt = time.perf_counter() - t0
+    n = case.x.shape[0]
+    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"all {n} rows of the logits workload, once ({dt:.1f} s; NumPy float64, "
+                      "element-wise, one thread)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-fused", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(vocab splits are emulated on one GPU); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from entropy_rlk_logprob_amd import binding
+    from entropy_rlk_logprob_amd import synthetic as S
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    lib = binding.load()
+    log("generating logits workload T=1024 V=151936")
+    case = S.logits_workload(2)
+    T, V = case.x.shape
+    x = torch.from_numpy(case.x).cuda()
+    t = torch.from_numpy(case.targets).cuda()
+    lp = torch.empty(T, dtype=torch.float32, device="cuda")
+    ent = torch.empty(T, dtype=torch.float32, device="cuda")
+
+    def step():
+        lib.logprob_from_logits(x, t, 1.0, 1, out=(lp, ent))
+
+    log(f"timing logits path: warmup {args.warmup}, steps {args.steps}")
+    k_ms, wall_ms, _ = time_calls(step, args.steps, args.warmup)
+    tokens_per_s = T / (wall_ms / 1e3)
+    alg_bytes = T * BYTES_PER_TOKEN_LOGITS
+    achieved = alg_bytes / (k_ms / 1e3) / 1e9
+    traffic = measured_traffic()
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": "row_reduce_kernel<8,true>",
+                "kernel_ms": round(k_ms, 5), "algorithmic_bytes": alg_bytes}
+
+    splits = {}
+    for sp in (2, 4, 8):
+        wsb = lib.workspace_bytes(binding.OP_FROM_LOGITS, T, V, 0, sp)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        fn = (lambda sp=sp, ws=ws: lib.logprob_from_logits(x, t, 1.0, sp, out=(lp, ent),
+                                                           workspace=ws))
+        ms, _, _ = time_calls(fn, max(5, args.steps // 5), 2)
+        splits[str(sp)] = round(ms, 5)
+    del x
+
+    fused = None
+    if not args.no_fused:
+        log("generating fused workload T=2048 d=4096 V=151936 (bf16)")
+        fc = S.fused_workload(4)
+        h = torch.from_numpy(fc.h_bits.view(np.int16)).cuda()
+        w = torch.from_numpy(fc.w_bits.view(np.int16)).cuda()
+        tt = torch.from_numpy(fc.targets).cuda()
+        Tf, d = fc.h_bits.shape
+        flp = torch.empty(Tf, dtype=torch.float32, device="cuda")
+        fent = torch.empty(Tf, dtype=torch.float32, device="cuda")
+        fws = torch.empty(lib.workspace_bytes(binding.OP_LINEAR, Tf, V, d, 1),
+                          dtype=torch.uint8, device="cuda")
+
+        def fstep():
+            lib.linear_logprob(h, w, tt, 1.0, 1, out=(flp, fent), workspace=fws)
+
+        fsteps = max(5, min(args.steps, 20))
+        log(f"timing fused path: steps {fsteps}")
+        f_ms, f_wall, _ = time_calls(fstep, fsteps, 2)
+        flops = 2.0 * Tf * V * d
+        tflops = flops / (f_ms / 1e3) / 1e12
+        fused = {"workload": S.WORKLOADS[4].name, "n_tokens": Tf, "hidden": d, "vocab": V,
+                 "ms_per_call": round(f_ms, 4), "tokens_per_s": round(Tf / (f_wall / 1e3), 1),
+                 "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
+                              "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                              "flops_per_call": flops}}
+        del h, w
+
+    cpu = None if args.no_cpu else cpu_baseline(case)
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": S.WORKLOADS[2].name, "n_tokens": T, "vocab": V,
+                   "vocab_splits": 1, "temperature": 1.0, "logits_dtype": "f32",
+                   "parallelism": "single-gpu"},
+        "backend": lib.backend_id(),
+        "roofline": roofline, "cpu_baseline": cpu, "fused": fused, "splits_ms": splits,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+"""Thin ctypes binding of librlk_logprob.so (include/rlk_logprob.h).
+
+Argument marshalling only: torch tensors provide device memory and the current HIP
+stream; every step of the computation runs in the library's kernels.  There is no
+fallback: if the library is missing or the device is not gfx950, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB_PATH = os.path.join(PKG, "librlk_logprob.so")
+HEADER = os.path.join(ROOT, "include", "rlk_logprob.h")
+
+RLK_OK = 0
+RLK_ERR_INVALID_ARGUMENT = 1
+RLK_ERR_UNSUPPORTED_DEVICE = 2
+RLK_ERR_WORKSPACE_TOO_SMALL = 3
+RLK_ERR_HIP = 4
+
+OP_FROM_LOGITS, OP_LINEAR, OP_ENTROPY = 0, 1, 2
+
+
+class RlkError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+_c_i64 = ctypes.c_int64
+_c_p = ctypes.c_void_p
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/rlk_logprob.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z_0-9]*\s*\*?\s*(rlk_[a-z_]+)\s*\(",
+                      text, flags=re.M)
+
+
+class Library:
+    """Loaded library with typed entry points."""
+
+    def __init__(self, path: str = LIB_PATH):
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is not built; run `python -m entropy_rlk_logprob_amd.build` "
+                "(there is no fallback implementation)")
+        self.path = path
+        self.lib = ctypes.CDLL(path)
+        L = self.lib
+        L.rlk_workspace_bytes.restype = ctypes.c_int
+        L.rlk_workspace_bytes.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, ctypes.c_int32,
+                                          ctypes.POINTER(ctypes.c_size_t)]
+        L.rlk_logprob_from_logits.restype = ctypes.c_int
+        L.rlk_logprob_from_logits.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_float,
+                                              ctypes.c_int32, _c_p, _c_p, _c_p, ctypes.c_size_t,
+                                              _c_p]
+        L.rlk_linear_logprob.restype = ctypes.c_int
+        L.rlk_linear_logprob.argtypes = [_c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p,
+                                         ctypes.c_float, ctypes.c_int32, _c_p, _c_p, _c_p,
+                                         ctypes.c_size_t, _c_p]
+        L.rlk_entropy.restype = ctypes.c_int
+        L.rlk_entropy.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, ctypes.c_float, ctypes.c_int32,
+                                  _c_p, _c_p, ctypes.c_size_t, _c_p]
+        L.rlk_status_string.restype = ctypes.c_char_p
+        L.rlk_status_string.argtypes = [ctypes.c_int]
+        L.rlk_backend_id.restype = ctypes.c_char_p
+        L.rlk_backend_id.argtypes = []
+
+    # ------------------------------------------------------------------ raw C calls
+    def status_string(self, status: int) -> str:
+        return self.lib.rlk_status_string(status).decode()
+
+    def backend_id(self) -> str:
+        return self.lib.rlk_backend_id().decode()
+
+    def check(self, status: int, what: str):
+        if status != RLK_OK:
+            raise RlkError(status, f"{what}: {self.status_string(status)}")
+
+    def workspace_bytes(self, op: int, n_tokens: int, vocab: int, hidden: int = 0,
+                        vocab_splits: int = 1) -> int:
+        out = ctypes.c_size_t(0)
+        st = self.lib.rlk_workspace_bytes(op, n_tokens, vocab, hidden, vocab_splits,
+                                          ctypes.byref(out))
+        self.check(st, "rlk_workspace_bytes")
+        return out.value
+
+    def logprob_from_logits_raw(self, *args) -> int:
+        return self.lib.rlk_logprob_from_logits(*args)
+
+    def linear_logprob_raw(self, *args) -> int:
+        return self.lib.rlk_linear_logprob(*args)
+
+    def entropy_raw(self, *args) -> int:
+        return self.lib.rlk_entropy(*args)
+
+    # ------------------------------------------------------------------ torch wrappers
+    @staticmethod
+    def _stream_handle(stream) -> int:
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream()
+        return int(s.cuda_stream)
+
+    @staticmethod
+    def _workspace(nbytes: int, device, workspace=None):
+        import torch
+        if nbytes == 0:
+            return None, 0
+        if workspace is not None:
+            if workspace.numel() * workspace.element_size() < nbytes:
+                raise RlkError(RLK_ERR_WORKSPACE_TOO_SMALL, "workspace tensor too small")
+            return workspace, workspace.numel() * workspace.element_size()
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return ws, nbytes
+
+    @staticmethod
+    def _ptr(t) -> int | None:
+        return None if t is None else t.data_ptr()
+
+    def logprob_from_logits(self, logits, targets, temperature: float = 1.0,
+                            vocab_splits: int = 1, with_entropy: bool = True, out=None,
+                            workspace=None, stream=None):
+        """logits: [T, >=V] float32 CUDA tensor (row stride = ld); targets: [T] int64."""
+        import torch
+        assert logits.dtype == torch.float32 and logits.dim() == 2 and logits.stride(1) == 1
+        assert targets.dtype == torch.int64 and targets.is_contiguous()
+        T, V = logits.shape
+        dev = logits.device
+        lp, ent = out if out is not None else (
+            torch.empty(T, dtype=torch.float32, device=dev),
+            torch.empty(T, dtype=torch.float32, device=dev) if with_entropy else None)
+        ws, wsb = self._workspace(self.workspace_bytes(OP_FROM_LOGITS, T, V, 0, vocab_splits),
+                                  dev, workspace)
+        st = self.lib.rlk_logprob_from_logits(
+            self._ptr(logits), logits.stride(0), T, V, self._ptr(targets), temperature,
+            vocab_splits, self._ptr(lp), self._ptr(ent), self._ptr(ws), wsb,
+            self._stream_handle(stream))
+        self.check(st, "rlk_logprob_from_logits")
+        return lp, ent
+
+    def entropy(self, logits, temperature: float = 1.0, vocab_splits: int = 1, out=None,
+                workspace=None, stream=None):
+        import torch
+        assert logits.dtype == torch.float32 and logits.dim() == 2 and logits.stride(1) == 1
+        T, V = logits.shape
+        ent = out if out is not None else torch.empty(T, dtype=torch.float32,
+                                                      device=logits.device)
+        ws, wsb = self._workspace(self.workspace_bytes(OP_ENTROPY, T, V, 0, vocab_splits),
+                                  logits.device, workspace)
+        st = self.lib.rlk_entropy(self._ptr(logits), logits.stride(0), T, V, temperature,
+                                  vocab_splits, self._ptr(ent), self._ptr(ws), wsb,
+                                  self._stream_handle(stream))
+        self.check(st, "rlk_entropy")
+        return ent
+
+    def linear_logprob(self, hidden, weight, targets, temperature: float = 1.0,
+                       vocab_splits: int = 1, with_entropy: bool = True, out=None,
+                       workspace=None, stream=None):
+        """hidden: [T, d] bf16 (or int16/uint16 bits); weight: [V, d] same; targets [T] int64."""
+        import torch
+        assert hidden.dim() == 2 and weight.dim() == 2
+        assert hidden.element_size() == 2 and weight.element_size() == 2
+        assert hidden.stride(1) == 1 and weight.stride(1) == 1
+        assert targets.dtype == torch.int64 and targets.is_contiguous()
+        T, d = hidden.shape
+        V, d2 = weight.shape
+        assert d == d2
+        dev = hidden.device
+        lp, ent = out if out is not None else (
+            torch.empty(T, dtype=torch.float32, device=dev),
+            torch.empty(T, dtype=torch.float32, device=dev) if with_entropy else None)
+        ws, wsb = self._workspace(self.workspace_bytes(OP_LINEAR, T, V, d, vocab_splits), dev,
+                                  workspace)
+        st = self.lib.rlk_linear_logprob(
+            self._ptr(hidden), hidden.stride(0), self._ptr(weight), weight.stride(0), T, d, V,
+            self._ptr(targets), temperature, vocab_splits, self._ptr(lp), self._ptr(ent),
+            self._ptr(ws), wsb, self._stream_handle(stream))
+        self.check(st, "rlk_linear_logprob")
+        return lp, ent
+
+
+_LIB: Library | None = None
+
+
+def load(path: str = LIB_PATH) -> Library:
+    """Load (once) and return the library; raises if it is not built."""
+    global _LIB
+    if _LIB is None or _LIB.path != path:
+        _LIB = Library(path)
+    return _LIB

@@ -1,0 +1,63 @@
+"""Build librlk_logprob.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+
+    python -m entropy_rlk_logprob_amd.build [--verbose]
+
+Flags that matter for the numerics: -ffp-contract=off (no implicit FMA contraction, so
+every rounding is the one the source spells out) and no fast-math.  Packed-fp32 VALU
+instruction selection is disabled for the device code.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "librlk_logprob.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+SOURCES = ["rlk_api.hip", "rlk_logits.hip", "rlk_linear.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found (ROCm is required to build the library)")
+    return path
+
+
+def flags() -> list[str]:
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        "-ffp-contract=off", "-fno-fast-math",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-function",
+        f"-I{INCLUDE}", f"-I{CSRC}",
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into one shared library; returns its path."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc()] + flags() + srcs + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the device-only feature flag; that warning is noise.
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="--verbose" in sys.argv))

@@ -1,0 +1,207 @@
+// C-ABI host layer: argument validation, workspace sizing, device check, launches.
+// Validation never touches the device and happens before anything is launched; there is
+// no fallback route -- an unsupported case is an error.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "rlk_launch.hpp"
+#include "rlk_logprob.h"
+#include "rlk_state.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+constexpr double kLog2e = 1.44269504088896340735992468100189214;
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxVocab = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxVocabLinear = int64_t(1) << 26;
+constexpr int64_t kMaxHidden = int64_t(1) << 20;
+// Row strides of the fused path: 256 rows x stride stays within 32-bit tile offsets.
+constexpr int64_t kMaxLdLinear = int64_t(1) << 22;
+
+rlk_status check_device() {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return RLK_ERR_UNSUPPORTED_DEVICE;
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return RLK_ERR_UNSUPPORTED_DEVICE;
+  if (dev >= kMaxDevices) return RLK_ERR_UNSUPPORTED_DEVICE;
+  int st = g_device_ok[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return RLK_ERR_UNSUPPORTED_DEVICE;
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_device_ok[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? RLK_OK : RLK_ERR_UNSUPPORTED_DEVICE;
+}
+
+bool valid_splits(int32_t s) { return s == 1 || s == 2 || s == 4 || s == 8; }
+
+bool valid_temperature(float t) { return std::isfinite(t) && t > 0.0f; }
+
+size_t logits_ws_bytes(int64_t T, int32_t S) {
+  return S > 1 ? (size_t)S * (size_t)T * sizeof(rlk::WireState) : 0;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shared validation of the logits-path calls.
+rlk_status validate_logits(const float* logits, int64_t ld, int64_t T, int64_t V,
+                           float temperature, int32_t S, void* ws, size_t ws_bytes) {
+  if (T < 0 || T > kMaxRows || V < 1 || V > kMaxVocab || ld < V) return RLK_ERR_INVALID_ARGUMENT;
+  if (T > 0 && !logits) return RLK_ERR_INVALID_ARGUMENT;
+  if (!valid_temperature(temperature) || !valid_splits(S)) return RLK_ERR_INVALID_ARGUMENT;
+  const size_t need = logits_ws_bytes(T, S);
+  if (need > 0 && (!ws || !aligned(ws, 256))) {
+    if (ws && !aligned(ws, 256)) return RLK_ERR_INVALID_ARGUMENT;
+    return RLK_ERR_WORKSPACE_TOO_SMALL;
+  }
+  if (ws_bytes < need) return RLK_ERR_WORKSPACE_TOO_SMALL;
+  return RLK_OK;
+}
+
+rlk_status run_logits(const float* logits, int64_t ld, int64_t T, int64_t V,
+                      const int64_t* targets, float temperature, int32_t S, float* lp, float* ent,
+                      void* ws, void* stream) {
+  rlk::LogitsArgs a;
+  a.X = logits;
+  a.ld = ld;
+  a.T = T;
+  a.V = V;
+  a.Vc = rlk::chunk_cols(V);
+  a.targets = targets;
+  a.beta = 1.0 / (double)temperature;
+  a.c = (float)(kLog2e / (double)temperature);
+  a.S = S;
+  a.vec = aligned(logits, 16) && (ld % 4 == 0);
+  a.lp = lp;
+  a.ent = ent;
+  a.ws = static_cast<rlk::WireState*>(ws);
+  const hipError_t e = rlk::launch_logits_path(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RLK_OK : RLK_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+rlk_status rlk_workspace_bytes(int op, int64_t n_tokens, int64_t vocab, int64_t hidden,
+                               int32_t vocab_splits, size_t* bytes_out) {
+  if (!bytes_out || n_tokens < 0 || n_tokens > kMaxRows || vocab < 1 ||
+      !valid_splits(vocab_splits))
+    return RLK_ERR_INVALID_ARGUMENT;
+  switch (op) {
+    case RLK_OP_FROM_LOGITS:
+    case RLK_OP_ENTROPY:
+      if (vocab > kMaxVocab) return RLK_ERR_INVALID_ARGUMENT;
+      *bytes_out = logits_ws_bytes(n_tokens, vocab_splits);
+      return RLK_OK;
+    case RLK_OP_LINEAR:
+      if (vocab > kMaxVocabLinear || hidden < 0) return RLK_ERR_INVALID_ARGUMENT;
+      *bytes_out = n_tokens == 0 ? 0
+                                 : rlk::linear_workspace_layout(n_tokens, vocab, vocab_splits).total;
+      return RLK_OK;
+    default:
+      return RLK_ERR_INVALID_ARGUMENT;
+  }
+}
+
+rlk_status rlk_logprob_from_logits(const float* logits, int64_t ld_logits, int64_t n_tokens,
+                                   int64_t vocab, const int64_t* target_ids, float temperature,
+                                   int32_t vocab_splits, float* logprob_out, float* entropy_out,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_tokens > 0 && (!target_ids || !logprob_out)) return RLK_ERR_INVALID_ARGUMENT;
+  rlk_status s = validate_logits(logits, ld_logits, n_tokens, vocab, temperature, vocab_splits,
+                                 workspace, workspace_bytes);
+  if (s != RLK_OK) return s;
+  if (n_tokens == 0) return RLK_OK;
+  s = check_device();
+  if (s != RLK_OK) return s;
+  return run_logits(logits, ld_logits, n_tokens, vocab, target_ids, temperature, vocab_splits,
+                    logprob_out, entropy_out, workspace, stream);
+}
+
+rlk_status rlk_entropy(const float* logits, int64_t ld_logits, int64_t n_tokens, int64_t vocab,
+                       float temperature, int32_t vocab_splits, float* entropy_out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_tokens > 0 && !entropy_out) return RLK_ERR_INVALID_ARGUMENT;
+  rlk_status s = validate_logits(logits, ld_logits, n_tokens, vocab, temperature, vocab_splits,
+                                 workspace, workspace_bytes);
+  if (s != RLK_OK) return s;
+  if (n_tokens == 0) return RLK_OK;
+  s = check_device();
+  if (s != RLK_OK) return s;
+  return run_logits(logits, ld_logits, n_tokens, vocab, nullptr, temperature, vocab_splits,
+                    nullptr, entropy_out, workspace, stream);
+}
+
+rlk_status rlk_linear_logprob(const uint16_t* hidden_bf16, int64_t ld_hidden,
+                              const uint16_t* weight_bf16, int64_t ld_weight, int64_t n_tokens,
+                              int64_t hidden_dim, int64_t vocab, const int64_t* target_ids,
+                              float temperature, int32_t vocab_splits, float* logprob_out,
+                              float* entropy_out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (n_tokens < 0 || n_tokens > kMaxRows || vocab < 1 || vocab > kMaxVocabLinear)
+    return RLK_ERR_INVALID_ARGUMENT;
+  if (hidden_dim < 64 || hidden_dim > kMaxHidden || hidden_dim % 64 != 0)
+    return RLK_ERR_INVALID_ARGUMENT;
+  if (ld_hidden < hidden_dim || ld_weight < hidden_dim || ld_hidden % 8 != 0 ||
+      ld_weight % 8 != 0 || ld_hidden > kMaxLdLinear || ld_weight > kMaxLdLinear)
+    return RLK_ERR_INVALID_ARGUMENT;
+  if (!valid_temperature(temperature) || !valid_splits(vocab_splits))
+    return RLK_ERR_INVALID_ARGUMENT;
+  if (n_tokens > 0) {
+    if (!hidden_bf16 || !weight_bf16 || !target_ids || !logprob_out)
+      return RLK_ERR_INVALID_ARGUMENT;
+    if (!aligned(hidden_bf16, 16) || !aligned(weight_bf16, 16)) return RLK_ERR_INVALID_ARGUMENT;
+    const size_t need = rlk::linear_workspace_layout(n_tokens, vocab, vocab_splits).total;
+    if (workspace && !aligned(workspace, 256)) return RLK_ERR_INVALID_ARGUMENT;
+    if (!workspace || workspace_bytes < need) return RLK_ERR_WORKSPACE_TOO_SMALL;
+  }
+  if (n_tokens == 0) return RLK_OK;
+  rlk_status s = check_device();
+  if (s != RLK_OK) return s;
+  rlk::LinearArgs a;
+  a.H = hidden_bf16;
+  a.W = weight_bf16;
+  a.ldh = ld_hidden;
+  a.ldw = ld_weight;
+  a.T = n_tokens;
+  a.d = hidden_dim;
+  a.V = vocab;
+  a.Vc = rlk::chunk_cols(vocab);
+  a.targets = target_ids;
+  a.beta = 1.0 / (double)temperature;
+  a.c = (float)(kLog2e / (double)temperature);
+  a.S = vocab_splits;
+  a.lp = logprob_out;
+  a.ent = entropy_out;
+  a.ws = workspace;
+  const hipError_t e = rlk::launch_linear_path(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RLK_OK : RLK_ERR_HIP;
+}
+
+const char* rlk_status_string(rlk_status status) {
+  switch (status) {
+    case RLK_OK: return "ok";
+    case RLK_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case RLK_ERR_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 required)";
+    case RLK_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case RLK_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* rlk_backend_id(void) { return "rlk.logprob.strict.gfx950.v1"; }
+
+}  // extern "C"

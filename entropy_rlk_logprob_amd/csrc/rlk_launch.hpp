@@ -1,0 +1,66 @@
+// Internal launch interface between the C-ABI host layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rlk {
+
+struct WireState;
+
+// Canonical vocabulary partition shared by both paths: 8 chunks of Vc columns,
+// Vc = 4 * ceil(ceil(V / 8) / 4).
+inline int64_t chunk_cols(int64_t V) {
+  const int64_t v8 = (V + 7) / 8;
+  return ((v8 + 3) / 4) * 4;
+}
+
+struct LogitsArgs {
+  const float* X;
+  int64_t ld, T, V, Vc;
+  const int64_t* targets;  // may be null (entropy only)
+  float c;                 // log2(e) / tau, rounded once to fp32
+  double beta;             // 1 / tau in fp64
+  int S;                   // vocab splits: 1, 2, 4, 8
+  bool vec;                // 16-byte loads legal (aligned base, ld % 4 == 0)
+  float* lp;               // may be null
+  float* ent;              // may be null
+  WireState* ws;           // S * T wire states when S > 1
+};
+
+hipError_t launch_logits_path(const LogitsArgs& a, hipStream_t stream);
+
+// Top log2(S) levels of the chunk tree over S shard states ([S][T] wire states), then
+// the fp64 finalize of every row.  Shared by both paths.
+hipError_t launch_shard_merge(const WireState* ws, int64_t T, const int64_t* targets, int64_t V,
+                              int64_t shard_cols, float c, double beta, int S, float* lp,
+                              float* ent, hipStream_t stream);
+
+struct LinearArgs {
+  const uint16_t* H;
+  const uint16_t* W;
+  int64_t ldh, ldw, T, d, V, Vc;
+  const int64_t* targets;
+  float c;
+  double beta;
+  int S;
+  float* lp;
+  float* ent;
+  void* ws;  // tile states, target logits, shard states
+};
+
+// Workspace layout of the fused path (offsets in bytes from the workspace base).
+struct LinearWorkspace {
+  int64_t tiles_per_chunk;  // ceil(Vc / kTileV)
+  int64_t n_tiles;          // 8 * tiles_per_chunk
+  size_t tile_states;       // n_tiles * T_pad TileState
+  size_t target_logit;      // T_pad floats
+  size_t shard_states;      // S * T WireState
+  size_t total;
+};
+
+LinearWorkspace linear_workspace_layout(int64_t T, int64_t V, int S);
+
+hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream);
+
+}  // namespace rlk

@@ -1,0 +1,347 @@
+// Fused path ("linear-logp"): logits = H W^T on bf16 MFMA tiles, folded tile by tile
+// into softmax states that never leave the chip as logits.
+//
+// Canonical order (independent of the number of rows, the row's place in a token tile,
+// the launch shape and the vocab split):
+//   * the 8 canonical chunks of Vc columns (as on the logits path); inside a chunk,
+//     vocabulary tiles of kTileV = 256 rows start at the chunk start, the last one short;
+//   * a logit is one fp32 accumulation over the hidden dimension in fixed order:
+//     64-wide K steps in increasing order, each four v_mfma_f32_32x32x16_bf16 steps
+//     (16 consecutive k each);
+//   * tile state of (token, tile): the 256 vocab rows split into two 128-row halves, each
+//     into four 32-row MFMA blocks; within a block a lane holds 16 rows
+//     8*(i/4) + 4*(lane/32) + (i%4), i = 0..15, which form one 16-element leaf (the same
+//     leaf as on the logits path: pairwise fp32 sums); the four leaves of a lane merge as
+//     ((0,1),(2,3)), then lane halves (lane < 32 first), then the two 128-row halves;
+//   * tiles of a chunk: balanced binary tree over tile index (padded with identities);
+//     chunks: ((0,1),(2,3)),((4,5),(6,7)), the top log2(S) levels in the shard merge.
+//
+// Workgroup: 8 waves, a 256 (vocab) x 256 (token) output tile, waves arranged 2 (vocab)
+// x 4 (token), each wave 128 x 64 = 4 x 2 MFMA blocks.  K step 64 with two LDS stages
+// (64 KiB each: the W and H slices with an XOR swizzle on 16-byte columns so that
+// ds_read_b128 of 8 consecutive rows hits distinct banks).  Workgroup ids are remapped
+// so that the token tiles of one vocabulary tile run back to back on the same XCD and
+// share its W slice in that XCD's L2.
+
+#include <hip/hip_runtime.h>
+
+#include "rlk_launch.hpp"
+#include "rlk_state.hpp"
+
+namespace rlk {
+
+namespace {
+
+constexpr int kTileV = 256;   // vocab rows per tile
+constexpr int kTileT = 256;   // tokens per tile
+constexpr int kBK = 64;       // hidden elements per K step
+constexpr int kThreads = 512; // 8 waves
+constexpr int kStageBytes = (kTileV + kTileT) * kBK * 2;  // 64 KiB
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+struct alignas(16) U4 {
+  uint32_t x, y, z, w;
+};
+
+// Byte offset of 16-byte column `c16` (0..7) of tile row `row` in a [rows][64] bf16 slab.
+__device__ __forceinline__ int swz(int row, int c16) { return row * 128 + ((c16 ^ (row & 7)) << 4); }
+
+__device__ __forceinline__ bf16x8 lds_frag(const char* base, int row, int c16) {
+  const U4 v = *reinterpret_cast<const U4*>(base + swz(row, c16));
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+struct TileGeom {
+  int64_t n_vt;       // vocabulary tiles (8 * tiles_per_chunk)
+  int64_t n_tt;       // token tiles
+  int64_t tpc;        // tiles per chunk
+  int64_t Vc, V, T;
+};
+
+__global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
+    const uint16_t* __restrict__ H, int64_t ldh, const uint16_t* __restrict__ W, int64_t ldw,
+    int64_t d, TileGeom g, const int64_t* __restrict__ targets, float c,
+    WireState* __restrict__ tile_states, float* __restrict__ target_logit) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+
+  // Remap the hardware id (dispatched round-robin over the 8 XCDs) so that logically
+  // consecutive tiles -- the token tiles of one vocabulary tile -- share an XCD.
+  const int64_t nb = g.n_vt * g.n_tt;
+  const int64_t per_xcd = (nb + 7) / 8;
+  const int64_t hw = blockIdx.x;
+  const int64_t logical = (hw % 8) * per_xcd + hw / 8;
+  if (logical >= nb) return;
+  const int64_t vt = logical / g.n_tt;
+  const int64_t tt = logical % g.n_tt;
+  const int64_t chunk = vt / g.tpc;
+  const int64_t kin = vt % g.tpc;
+  const int64_t chunk_lo = min(chunk * g.Vc, g.V);
+  const int64_t chunk_hi = min(chunk_lo + g.Vc, g.V);
+  const int64_t v_lo = chunk_lo + kin * kTileV;
+  const int64_t v_hi = min(v_lo + (int64_t)kTileV, chunk_hi);
+  const int64_t t_lo = tt * kTileT;
+  if (v_lo >= v_hi) {
+    // Empty tile (short chunk): identity states so that the tile tree sees no data.
+    for (int j = threadIdx.x; j < kTileT; j += kThreads) {
+      const int64_t tok = t_lo + j;
+      if (tok < g.T) tile_states[vt * g.T + tok] = to_wire(identity_state(), 0.0f);
+    }
+    return;
+  }
+
+  const int n_valid = (int)(v_hi - v_lo);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wv = wave >> 2;  // vocab half (0, 1)
+  const int wt = wave & 3;   // token quarter (0..3)
+
+  // Global -> LDS: direct 16-byte-per-lane loads into LDS (global_load_lds_dwordx4).  One
+  // wave instruction fills one 1 KiB block = 8 slab rows; lane l writes physical column
+  // l % 8 of row l / 8 in the block, so it fetches logical column (l % 8) ^ (l / 8) --
+  // the XOR swizzle is applied on the source side.  Wave w fills blocks 4 w .. 4 w + 3
+  // of both slabs.  Offsets are tile-relative on workgroup-uniform bases; rows beyond
+  // the valid range are clamped to the last valid row (masked later, never stored).
+  const uint16_t* __restrict__ Wt = W + v_lo * ldw;
+  const uint16_t* __restrict__ Ht = H + t_lo * ldh;
+  const int w_last = (int)min(g.V - 1 - v_lo, (int64_t)(kTileV - 1));
+  const int h_last = (int)min(g.T - 1 - t_lo, (int64_t)(kTileT - 1));
+  const int src_c16 = (lane & 7) ^ (lane >> 3);
+  int woff[4], hoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (wave * 4 + i) * 8 + (lane >> 3);
+    woff[i] = min(row, w_last) * (int)ldw + src_c16 * 8;
+    hoff[i] = min(row, h_last) * (int)ldh + src_c16 * 8;
+  }
+  auto issue_stage = [&](int64_t k0, int stage) {
+    char* wb = smem + stage * kStageBytes + wave * 4 * 1024;
+    char* hb = smem + stage * kStageBytes + kTileV * kBK * 2 + wave * 4 * 1024;
+    const uint16_t* wk = Wt + k0;
+    const uint16_t* hk = Ht + k0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(wk + woff[i]),
+                                       (__attribute__((address_space(3))) void*)(wb + i * 1024),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(hk + hoff[i]),
+                                       (__attribute__((address_space(3))) void*)(hb + i * 1024),
+                                       16, 0, 0);
+    }
+  };
+
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+
+  const int nk = (int)(d / kBK);
+  issue_stage(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const int frow = lane & 31;
+  const int fhalf = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    // The other stage was last read in iteration kt - 1, which every wave has left.
+    if (kt + 1 < nk) issue_stage((int64_t)(kt + 1) * kBK, (kt + 1) & 1);
+    const char* wb = smem + (kt & 1) * kStageBytes;
+    const char* hb = wb + kTileV * kBK * 2;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c16 = 2 * ks + fhalf;
+      bf16x8 af[4], bfr[2];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) af[a] = lds_frag(wb, wv * 128 + a * 32 + frow, c16);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) bfr[b] = lds_frag(hb, wt * 64 + b * 32 + frow, c16);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  // Each lane owns tokens wt*64 + b*32 + (lane%32), b = 0, 1, and for each of them the
+  // 64 vocab rows wv*128 + a*32 + 8*(i/4) + 4*(lane/32) + (i%4).
+  State half_state[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int tok_in_tile = wt * 64 + b * 32 + frow;
+    const int64_t tok = t_lo + tok_in_tile;
+    const int64_t tgt = (tok < g.T && targets) ? targets[tok] : -1;
+    // Target row relative to this tile, or -1 when the target is not in the tile.
+    const int tloc = (tgt >= v_lo && tgt < v_hi) ? (int)(tgt - v_lo) : -1;
+    State leaf[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int vr = wv * 128 + a * 32 + 8 * (i >> 2) + 4 * fhalf + (i & 3);
+        v[i] = (vr < n_valid) ? acc[a][b][i] : kNegInf;
+        if (vr == tloc) target_logit[tok] = acc[a][b][i];
+      }
+      leaf[a] = leaf16(v, c);
+    }
+    State st = rlk_merge(rlk_merge(leaf[0], leaf[1], c), rlk_merge(leaf[2], leaf[3], c), c);
+    const State o = shfl_xor_state(st, 32);
+    half_state[b] = fhalf ? rlk_merge(o, st, c) : rlk_merge(st, o, c);
+  }
+
+  // Cross-half merge through LDS: the upper vocab half (wv = 1) publishes its states,
+  // the lower half merges (lower range first) and stores the tile state.
+  State* xch = reinterpret_cast<State*>(smem);
+  if (wv == 1 && fhalf == 0) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) xch[wt * 64 + b * 32 + frow] = half_state[b];
+  }
+  __syncthreads();
+  if (wv == 0 && fhalf == 0) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int tok_in_tile = wt * 64 + b * 32 + frow;
+      const int64_t tok = t_lo + tok_in_tile;
+      if (tok < g.T) {
+        const State r = rlk_merge(half_state[b], xch[tok_in_tile], c);
+        tile_states[vt * g.T + tok] = to_wire(r, 0.0f);
+      }
+    }
+  }
+}
+
+// Tiles of each chunk -> chunk states (balanced tree over tile index), chunks of a
+// shard -> shard state (tree8), then either the fp64 finalize (S = 1) or the shard's
+// wire state for the cross-shard merge.  Block: (256 / CPS) tokens x CPS chunks.
+template <int CPS>
+__global__ __launch_bounds__(256) void tile_tree_kernel(
+    const WireState* __restrict__ tile_states, const float* __restrict__ target_logit,
+    TileGeom g, const int64_t* __restrict__ targets, float c, double beta,
+    float* __restrict__ lp_out, float* __restrict__ ent_out, WireState* __restrict__ shard_ws) {
+  constexpr int TPB = 256 / CPS;
+  const int j = threadIdx.x % TPB;
+  const int ci = threadIdx.x / TPB;
+  const int shard = blockIdx.y;
+  const int64_t tok = (int64_t)blockIdx.x * TPB + j;
+  const int64_t chunk = (int64_t)shard * CPS + ci;
+  __shared__ State cs[CPS][TPB];
+
+  State r = identity_state();
+  if (tok < g.T) {
+    State stk[24];
+    int top = 0;
+    const WireState* base = tile_states + chunk * g.tpc * g.T + tok;
+    for (int64_t k = 0; k < g.tpc; ++k) {
+      State cur = from_wire(base[k * g.T]);
+      for (int64_t b = k; b & 1; b >>= 1) cur = rlk_merge(stk[--top], cur, c);
+      stk[top++] = cur;
+    }
+    r = stk[--top];
+    while (top > 0) r = rlk_merge(stk[--top], r, c);
+  }
+  cs[ci][j] = r;
+  __syncthreads();
+  if (ci != 0 || tok >= g.T) return;
+  State v[CPS];
+#pragma unroll
+  for (int i = 0; i < CPS; ++i) v[i] = cs[i][j];
+  const State root = tree8(v, CPS, c);
+  const int64_t t = targets ? targets[tok] : -1;
+  if constexpr (CPS == 8) {
+    const bool has = (t >= 0) && (t < g.V);
+    const float xt = has ? target_logit[tok] : 0.0f;
+    rlk_finalize(root, xt, has, beta, lp_out ? lp_out + tok : nullptr,
+                 ent_out ? ent_out + tok : nullptr);
+  } else {
+    const int64_t s_lo = min((int64_t)shard * CPS * g.Vc, g.V);
+    const int64_t s_hi = min(s_lo + (int64_t)CPS * g.Vc, g.V);
+    const bool mine = (t >= s_lo) && (t < s_hi);
+    shard_ws[(int64_t)shard * g.T + tok] = to_wire(root, mine ? target_logit[tok] : 0.0f);
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+LinearWorkspace linear_workspace_layout(int64_t T, int64_t V, int S) {
+  LinearWorkspace L;
+  const int64_t Vc = chunk_cols(V);
+  L.tiles_per_chunk = (Vc + kTileV - 1) / kTileV;
+  L.n_tiles = 8 * L.tiles_per_chunk;
+  size_t off = 0;
+  L.tile_states = off;
+  off += align256((size_t)L.n_tiles * (size_t)T * sizeof(WireState));
+  L.target_logit = off;
+  off += align256((size_t)T * sizeof(float));
+  L.shard_states = off;
+  off += (S > 1) ? align256((size_t)S * (size_t)T * sizeof(WireState)) : 0;
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream) {
+  const LinearWorkspace L = linear_workspace_layout(a.T, a.V, a.S);
+  TileGeom g;
+  g.tpc = L.tiles_per_chunk;
+  g.n_vt = L.n_tiles;
+  g.n_tt = (a.T + kTileT - 1) / kTileT;
+  g.Vc = a.Vc;
+  g.V = a.V;
+  g.T = a.T;
+  char* base = static_cast<char*>(a.ws);
+  const int64_t nb = g.n_vt * g.n_tt;
+  const int64_t nb_pad = ((nb + 7) / 8) * 8;
+  hipLaunchKernelGGL(linear_tile_kernel, dim3((unsigned)nb_pad), dim3(kThreads), 0, stream, a.H,
+                     a.ldh, a.W, a.ldw, a.d, g, a.targets, a.c,
+                     reinterpret_cast<WireState*>(base + L.tile_states),
+                     reinterpret_cast<float*>(base + L.target_logit));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const WireState* tiles = reinterpret_cast<const WireState*>(base + L.tile_states);
+  const float* tl = reinterpret_cast<const float*>(base + L.target_logit);
+  WireState* sws = reinterpret_cast<WireState*>(base + L.shard_states);
+  switch (a.S) {
+    case 1: {
+      const dim3 grid((unsigned)((a.T + 31) / 32), 1);
+      hipLaunchKernelGGL((tile_tree_kernel<8>), grid, dim3(256), 0, stream, tiles, tl, g,
+                         a.targets, a.c, a.beta, a.lp, a.ent, sws);
+      return hipGetLastError();
+    }
+    case 2: {
+      const dim3 grid((unsigned)((a.T + 63) / 64), 2);
+      hipLaunchKernelGGL((tile_tree_kernel<4>), grid, dim3(256), 0, stream, tiles, tl, g,
+                         a.targets, a.c, a.beta, a.lp, a.ent, sws);
+      break;
+    }
+    case 4: {
+      const dim3 grid((unsigned)((a.T + 127) / 128), 4);
+      hipLaunchKernelGGL((tile_tree_kernel<2>), grid, dim3(256), 0, stream, tiles, tl, g,
+                         a.targets, a.c, a.beta, a.lp, a.ent, sws);
+      break;
+    }
+    case 8: {
+      const dim3 grid((unsigned)((a.T + 255) / 256), 8);
+      hipLaunchKernelGGL((tile_tree_kernel<1>), grid, dim3(256), 0, stream, tiles, tl, g,
+                         a.targets, a.c, a.beta, a.lp, a.ent, sws);
+      break;
+    }
+    default:
+      return hipErrorInvalidValue;
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_shard_merge(sws, a.T, a.targets, a.V, (int64_t)(8 / a.S) * a.Vc, a.c, a.beta,
+                            a.S, a.lp, a.ent, stream);
+}
+
+}  // namespace rlk

@@ -1,0 +1,198 @@
+// Logits path: streaming fixed-order row reducer and the vocab-shard merge.
+//
+// Canonical order for a row of V fp32 logits (the contract that makes results independent
+// of rows-per-call, row order, repeats and vocab split):
+//   * 8 chunks of Vc = 4 * ceil(ceil(V / 8) / 4) columns (the last ones short or empty);
+//   * within a chunk, quad q covers chunk columns [4q, 4q+4) and belongs to lane q % 64;
+//     a lane's quads k = 0, 1, 2, ... (q = lane + 64 k) are grouped four at a time into
+//     16-element leaves;
+//   * leaf: m = max of its 16 values, then fp32 2^{c (x - m)} terms summed pairwise
+//     (within each quad, then quad pairs); leaves are folded into the lane's fp64 state
+//     in increasing k with rlk_merge;
+//   * lanes: xor-butterfly (32, 16, 8, 4, 2, 1); chunks: ((0,1),(2,3)),((4,5),(6,7)).
+// A vocab shard (split count S) owns 8/S consecutive chunks, reduces them in one
+// workgroup exactly as the unsplit case does, and hands its state to the merge kernel,
+// which applies the top S-leaf part of the same chunk tree.
+//
+// Layout and launch: one workgroup per (row, shard), one wave per chunk; each lane
+// streams 16-byte loads whose 64 lanes cover 1 KiB of contiguous HBM per instruction.
+// The loads carry the non-temporal hint: every logit is read exactly once.
+
+#include "rlk_launch.hpp"
+#include "rlk_state.hpp"
+
+namespace rlk {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct Quad4 {
+  float v[16];
+};
+
+template <bool VEC>
+__device__ __forceinline__ void load_quad(const float* __restrict__ p, int q, float* dst) {
+  if constexpr (VEC) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + q);
+    dst[0] = v.x;
+    dst[1] = v.y;
+    dst[2] = v.z;
+    dst[3] = v.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[j] = __builtin_nontemporal_load(p + 4 * q + j);
+  }
+}
+
+// Group g of a lane: quads q = lane + 64 * (4 g + i), i = 0..3, all inside the chunk.
+template <bool VEC>
+__device__ __forceinline__ void load_group_full(const float* __restrict__ p, int lane, int g,
+                                                Quad4& out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load_quad<VEC>(p, lane + 64 * (4 * g + i), out.v + 4 * i);
+}
+
+// Same, with columns at or beyond n replaced by -inf (the identity's contribution).
+__device__ __forceinline__ void load_group_masked(const float* __restrict__ p, int lane, int g,
+                                                  int n, Quad4& out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = lane + 64 * (4 * g + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = 4 * q + j;
+      out.v[4 * i + j] = (col < n) ? __builtin_nontemporal_load(p + col) : kNegInf;
+    }
+  }
+}
+
+// One workgroup = one (row, shard); WAVES = 8 / S chunks per shard, one wave per chunk.
+template <int WAVES, bool VEC>
+__global__ __launch_bounds__(64 * WAVES) void row_reduce_kernel(
+    const float* __restrict__ X, int64_t ld, int64_t T, int64_t V, int64_t Vc,
+    const int64_t* __restrict__ targets, float c, double beta, float* __restrict__ lp_out,
+    float* __restrict__ ent_out, WireState* __restrict__ ws) {
+  const int64_t row = blockIdx.x;
+  const int shard = blockIdx.y;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t chunk = (int64_t)shard * WAVES + wave;
+  const int64_t lo = min(chunk * Vc, V);
+  const int64_t hi = min(lo + Vc, V);
+  const int n = (int)(hi - lo);
+  const float* __restrict__ p = X + row * ld + lo;
+
+  State st = identity_state();
+  const int n_groups = (((n + 3) >> 2) + 255) >> 8;  // ceil(ceil(n/4) / 256)
+  const int n_full = (n >> 2) >> 8;                   // groups with every column inside
+  if (n_full > 0) {
+    Quad4 cur, nxt;
+    load_group_full<VEC>(p, lane, 0, cur);
+    for (int g = 0; g < n_full; ++g) {
+      if (g + 1 < n_full) load_group_full<VEC>(p, lane, g + 1, nxt);
+      st = rlk_merge(st, leaf16(cur.v, c), c);
+      cur = nxt;
+    }
+  }
+  for (int g = n_full; g < n_groups; ++g) {
+    Quad4 q;
+    load_group_masked(p, lane, g, n, q);
+    st = rlk_merge(st, leaf16(q.v, c), c);
+  }
+  st = wave_tree(st, c);
+
+  __shared__ State chunk_state[WAVES];
+  if (lane == 0) chunk_state[wave] = st;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+
+  const State r = tree8(chunk_state, WAVES, c);
+  const int64_t t = targets ? targets[row] : -1;
+  if constexpr (WAVES == 8) {
+    const bool has = (t >= 0) && (t < V);
+    const float xt = has ? X[row * ld + t] : 0.0f;
+    rlk_finalize(r, xt, has, beta, lp_out ? lp_out + row : nullptr,
+                 ent_out ? ent_out + row : nullptr);
+  } else {
+    const int64_t s_lo = min((int64_t)shard * WAVES * Vc, V);
+    const int64_t s_hi = min(s_lo + (int64_t)WAVES * Vc, V);
+    const bool mine = (t >= s_lo) && (t < s_hi);
+    const float xt = mine ? X[row * ld + t] : 0.0f;
+    ws[(int64_t)shard * T + row] = to_wire(r, xt);
+  }
+}
+
+// Top of the chunk tree across S shard states, then the fp64 finalize; one thread per row.
+template <int S>
+__global__ __launch_bounds__(256) void shard_merge_kernel(
+    const WireState* __restrict__ ws, int64_t T, const int64_t* __restrict__ targets, int64_t V,
+    int64_t shard_cols, float c, double beta, float* __restrict__ lp_out,
+    float* __restrict__ ent_out) {
+  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= T) return;
+  State v[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) v[s] = from_wire(ws[(int64_t)s * T + row]);
+  const State r = tree8(v, S, c);
+  const int64_t t = targets ? targets[row] : -1;
+  const bool has = (t >= 0) && (t < V);
+  const int64_t owner = has ? (t / shard_cols) : 0;
+  const float xt = has ? ws[owner * T + row].xt : 0.0f;
+  rlk_finalize(r, xt, has, beta, lp_out ? lp_out + row : nullptr,
+               ent_out ? ent_out + row : nullptr);
+}
+
+template <int WAVES>
+hipError_t launch_rows(const LogitsArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.T, (unsigned)(8 / WAVES));
+  const dim3 block(64 * WAVES);
+  if (a.vec)
+    hipLaunchKernelGGL((row_reduce_kernel<WAVES, true>), grid, block, 0, stream, a.X, a.ld, a.T,
+                       a.V, a.Vc, a.targets, a.c, a.beta, a.lp, a.ent, a.ws);
+  else
+    hipLaunchKernelGGL((row_reduce_kernel<WAVES, false>), grid, block, 0, stream, a.X, a.ld, a.T,
+                       a.V, a.Vc, a.targets, a.c, a.beta, a.lp, a.ent, a.ws);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_logits_path(const LogitsArgs& a, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  switch (a.S) {
+    case 1: return launch_rows<8>(a, stream);
+    case 2: e = launch_rows<4>(a, stream); break;
+    case 4: e = launch_rows<2>(a, stream); break;
+    case 8: e = launch_rows<1>(a, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  return launch_shard_merge(a.ws, a.T, a.targets, a.V, (int64_t)(8 / a.S) * a.Vc, a.c, a.beta,
+                            a.S, a.lp, a.ent, stream);
+}
+
+hipError_t launch_shard_merge(const WireState* ws, int64_t T, const int64_t* targets, int64_t V,
+                              int64_t shard_cols, float c, double beta, int S, float* lp,
+                              float* ent, hipStream_t stream) {
+  const dim3 grid((unsigned)((T + 255) / 256));
+  switch (S) {
+    case 2:
+      hipLaunchKernelGGL((shard_merge_kernel<2>), grid, dim3(256), 0, stream, ws, T, targets, V,
+                         shard_cols, c, beta, lp, ent);
+      break;
+    case 4:
+      hipLaunchKernelGGL((shard_merge_kernel<4>), grid, dim3(256), 0, stream, ws, T, targets, V,
+                         shard_cols, c, beta, lp, ent);
+      break;
+    case 8:
+      hipLaunchKernelGGL((shard_merge_kernel<8>), grid, dim3(256), 0, stream, ws, T, targets, V,
+                         shard_cols, c, beta, lp, ent);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rlk

@@ -1,0 +1,159 @@
+// Device-side reduction state shared by every kernel of the library.
+//
+// A state summarises the tempered softmax over a contiguous vocabulary range R:
+//     m = max_{i in R} x_i                       (raw logit, fp32)
+//     s = sum_{i in R} 2^{a_i}                   (fp64 once above a leaf)
+//     u = sum_{i in R} 2^{a_i} * a_i             (fp64 once above a leaf)
+// with a_i = c * (x_i - m) and c = log2(e) / tau rounded once to fp32 on the host.
+// Identity: (-inf, 0, 0).  The selected-token logprob and the entropy of a full row are
+//     logprob = (x_t - m) / tau - ln s,     entropy = ln s - ln(2) * u / s,
+// evaluated in fp64 (finalize) from the root state.
+//
+// Strictness: every merge in every kernel goes through rlk_merge() below, always with
+// the lower vocabulary range as its first operand, and the library is compiled with
+// -ffp-contract=off so that no compiler contraction changes a rounding.  Trees are
+// fixed functions of the vocabulary position only, never of the number of rows, the
+// row's place in a tile, the launch shape or the vocab split count.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rlk {
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kMaxFloat = 3.40282346638528859811704183484516925e+38f;
+constexpr double kLn2 = 0.693147180559945309417232121458176568;
+
+// 2^x on the hardware transcendental unit (v_exp_f32): exact at x = 0, 0 at x = -inf.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+struct State {
+  float m;
+  double s;
+  double u;
+};
+
+// Exchange / workspace format of a state plus the captured target logit (24 bytes).
+struct alignas(8) WireState {
+  float m;
+  float xt;   // target logit if the target lies in this range, else unused
+  double s;
+  double u;
+};
+
+__device__ __forceinline__ State identity_state() { return State{kNegInf, 0.0, 0.0}; }
+
+// Merge of two states over adjacent ranges, `a` covering the lower vocabulary indices.
+// Only the operand with the smaller max is rescaled (2^0 = 1 exactly for the other),
+// a range of all -inf contributes nothing, and NaN in s or u propagates.
+__device__ __forceinline__ State rlk_merge(const State& a, const State& b, float c) {
+  const bool a_ge = a.m >= b.m;
+  const float M = a_ge ? a.m : b.m;
+  const float lo = a_ge ? b.m : a.m;
+  const float Mref = (M == kNegInf) ? 0.0f : M;
+  const float dlo = (lo - Mref) * c;           // <= 0, or -inf, or NaN if M = +inf
+  const float elo = exp2_hw(dlo);
+  const float dlo_c = fmaxf(dlo, -kMaxFloat);  // keeps 0 * (-inf) out of u
+  const double ea = a_ge ? 1.0 : (double)elo;
+  const double eb = a_ge ? (double)elo : 1.0;
+  const double da = a_ge ? 0.0 : (double)dlo_c;
+  const double db = a_ge ? (double)dlo_c : 0.0;
+  State r;
+  r.m = M;
+  r.s = fma(a.s, ea, b.s * eb);
+  const double ua = fma(da, a.s, a.u);
+  const double ub = fma(db, b.s, b.u);
+  r.u = fma(ua, ea, ub * eb);
+  return r;
+}
+
+// Final per-row evaluation in fp64 from the root state; one rounding to fp32.
+// beta = 1/tau in fp64.  has_target: the target lies in [0, V) (xt is its logit).
+__device__ __forceinline__ void rlk_finalize(const State& st, float xt, bool has_target,
+                                             double beta, float* lp, float* ent) {
+  const double qnan = __builtin_nan("");
+  const bool ok = (st.m != kNegInf) && (st.s > 0.0) && (st.s < __builtin_inf()) &&
+                  (st.u == st.u);
+  double l = ok ? log(st.s) : qnan;
+  double e = ok ? (l - kLn2 * (st.u / st.s)) : qnan;
+  double p = (ok && has_target) ? (beta * ((double)xt - (double)st.m) - l) : qnan;
+  if (lp) *lp = (float)p;
+  if (ent) *ent = (float)e;
+}
+
+__device__ __forceinline__ State from_wire(const WireState& w) { return State{w.m, w.s, w.u}; }
+
+__device__ __forceinline__ WireState to_wire(const State& s, float xt) {
+  WireState w;
+  w.m = s.m;
+  w.xt = xt;
+  w.s = s.s;
+  w.u = s.u;
+  return w;
+}
+
+// Leaf of 16 fp32 values v[0..15] (four quads of four): exact max m, then the fp32 terms
+// 2^a and 2^a * a with a = c (v - m) summed pairwise, within each quad and then across
+// quad pairs.  -inf entries contribute nothing; a leaf of only -inf is (-inf, 0, 0).
+__device__ __forceinline__ State leaf16(const float* v, float c) {
+  const float m0 = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+  const float m1 = fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7]));
+  const float m2 = fmaxf(fmaxf(v[8], v[9]), fmaxf(v[10], v[11]));
+  const float m3 = fmaxf(fmaxf(v[12], v[13]), fmaxf(v[14], v[15]));
+  const float mg = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+  const float mref = (mg == kNegInf) ? 0.0f : mg;
+  float e[16], t[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float a = (v[i] - mref) * c;
+    e[i] = exp2_hw(a);
+    t[i] = e[i] * fmaxf(a, -kMaxFloat);
+  }
+  float sq[4], uq[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sq[j] = (e[4 * j] + e[4 * j + 1]) + (e[4 * j + 2] + e[4 * j + 3]);
+    uq[j] = (t[4 * j] + t[4 * j + 1]) + (t[4 * j + 2] + t[4 * j + 3]);
+  }
+  State r;
+  r.m = mg;
+  r.s = (double)((sq[0] + sq[1]) + (sq[2] + sq[3]));
+  r.u = (double)((uq[0] + uq[1]) + (uq[2] + uq[3]));
+  return r;
+}
+
+// Wave-wide shuffle of a state (64 lanes).
+__device__ __forceinline__ State shfl_xor_state(const State& s, int mask) {
+  State r;
+  r.m = __shfl_xor(s.m, mask, 64);
+  r.s = __shfl_xor(s.s, mask, 64);
+  r.u = __shfl_xor(s.u, mask, 64);
+  return r;
+}
+
+// Fixed xor-butterfly over the 64 lanes of a wave (strides 32, 16, 8, 4, 2, 1).  At each
+// level both partners evaluate the same merge with the lower lane's state first, so all
+// lanes end with identical bits.
+__device__ __forceinline__ State wave_tree(State st, float c) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    State o = shfl_xor_state(st, off);
+    st = (lane & off) ? rlk_merge(o, st, c) : rlk_merge(st, o, c);
+  }
+  return st;
+}
+
+// Balanced tree over n = 1, 2, 4 or 8 consecutive states (lower index first):
+// ((0,1),(2,3)),((4,5),(6,7)).
+__device__ __forceinline__ State tree8(const State* v, int n, float c) {
+  if (n == 1) return v[0];
+  if (n == 2) return rlk_merge(v[0], v[1], c);
+  if (n == 4) return rlk_merge(rlk_merge(v[0], v[1], c), rlk_merge(v[2], v[3], c), c);
+  State l = rlk_merge(rlk_merge(v[0], v[1], c), rlk_merge(v[2], v[3], c), c);
+  State r = rlk_merge(rlk_merge(v[4], v[5], c), rlk_merge(v[6], v[7], c), c);
+  return rlk_merge(l, r, c);
+}
+
+}  // namespace rlk

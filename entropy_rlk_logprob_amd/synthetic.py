@@ -89,7 +89,7 @@ def uniform_targets(rng: np.random.Generator, n: int, vocab: int) -> np.ndarray:
 
 
 def gumbel_max_targets(rng: np.random.Generator, x: np.ndarray, temperature: float = 1.0,
-                       block: int = 64) -> np.ndarray:
+                       block: int = 8) -> np.ndarray:
     """Draw one id per row with probability proportional to exp(x/tau).
 
     Gumbel-max: argmax_i(x_i/tau + G_i) with G_i = -log(-log U_i) is an exact sample

@@ -1,0 +1,132 @@
+/*
+ * rlk_logprob.h -- strict selected-token log-probability and per-token entropy on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes.  For every row r of logits x (given directly, or as the
+ * LM-head projection x = H W^T of a bf16 hidden state) and a temperature tau:
+ *
+ *     logprob[r] = x_t/tau - log sum_i exp(x_i/tau)           (t = target_ids[r])
+ *     entropy[r] = - sum_i p_i log p_i,  p_i = softmax(x/tau)_i  (natural log, 0 log 0 = 0)
+ *
+ * over the FULL vocabulary.  This is the "selected logprob" of each response row named
+ * by the RL-Kernel issue #342 runbook "Strict R/R trace and operator ablation runbook"
+ * (section 2: per-row selected-logprob comparison between training and rollout), the
+ * per-token entropy behind the RL-Kernel h100-pcp.json page's train/entropy_loss, and
+ * the "linear_logp" operator (LM-head projection fused with the logprob) whose backend
+ * id "rlkernel.linear_logp.bitwise.v1" appears in that page's runtime readbacks.
+ *
+ * Strictness contract (the checks of the RL-Kernel Qwen3-Next logprob prior-art report:
+ * tp4_equals_tp1, batch_bitwise, distinct_results_in_repeats):
+ *   - results are bitwise identical whatever the number of rows, their order, which
+ *     other rows share the call, the repeat, and the vocab split count (1, 2, 4 or 8
+ *     contiguous vocabulary shards, each reduced on its own as a vocab-parallel rank
+ *     would, then merged in one fixed tree);
+ *   - there are no atomics and no data-dependent reduction order;
+ *   - there is no fallback path: an unsupported case returns an error.
+ *
+ * Conventions for every call:
+ *   - all tensor pointers are DEVICE pointers owned by the caller, row-major;
+ *     inputs are never modified; outputs are fp32;
+ *   - every call is asynchronous on `stream` (a hipStream_t passed as void*, NULL =
+ *     the default stream); it never allocates, never synchronizes and never reads
+ *     device memory on the host; results are valid once the stream has reached the
+ *     point of the call;
+ *   - arguments are validated on the host before anything is launched; on error
+ *     nothing is launched and no output is written;
+ *   - n_tokens == 0 returns RLK_OK and launches nothing;
+ *   - a target id outside [0, vocab) gives a NaN logprob for that row (its entropy is
+ *     still computed); a NaN or +inf logit anywhere in a row, or a row whose logits are
+ *     all -inf, gives NaN for both outputs of that row; -inf logits are tokens of
+ *     probability zero;
+ *   - the current HIP device must be a gfx950 GPU, otherwise
+ *     RLK_ERR_UNSUPPORTED_DEVICE;
+ *   - calls on different streams may run concurrently if they use distinct workspaces.
+ */
+#ifndef RLK_LOGPROB_H
+#define RLK_LOGPROB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RLK_OK = 0,
+  RLK_ERR_INVALID_ARGUMENT = 1,  /* null pointer, bad size, bad stride, bad temperature,
+                                    vocab_splits not in {1,2,4,8}, bad op code           */
+  RLK_ERR_UNSUPPORTED_DEVICE = 2,/* no HIP device, or the current device is not gfx950  */
+  RLK_ERR_WORKSPACE_TOO_SMALL = 3,/* workspace_bytes below rlk_workspace_bytes()        */
+  RLK_ERR_HIP = 4                /* a HIP runtime call or kernel launch failed          */
+} rlk_status;
+
+/* Operation codes for rlk_workspace_bytes. */
+#define RLK_OP_FROM_LOGITS 0
+#define RLK_OP_LINEAR 1
+#define RLK_OP_ENTROPY 2
+
+/*
+ * Device workspace, in bytes, that the call `op` needs for these sizes.  Pure host
+ * arithmetic (no device access).  `hidden` is ignored unless op == RLK_OP_LINEAR.
+ * The workspace must be 256-byte aligned; its contents on entry do not matter.
+ * Returns RLK_ERR_INVALID_ARGUMENT for a bad op, negative sizes or a bad split count.
+ */
+rlk_status rlk_workspace_bytes(int op, int64_t n_tokens, int64_t vocab, int64_t hidden,
+                               int32_t vocab_splits, size_t* bytes_out);
+
+/*
+ * Selected-token logprob (and optionally entropy) from precomputed fp32 logits.
+ *   logits        [n_tokens, ld_logits] fp32, first `vocab` columns used, ld_logits >= vocab
+ *   target_ids    [n_tokens] int64
+ *   temperature   finite, > 0 (the softmax is of logits / temperature)
+ *   vocab_splits  1, 2, 4 or 8: number of contiguous vocabulary shards reduced separately
+ *                 and merged (the result bits do not depend on it)
+ *   logprob_out   [n_tokens] fp32
+ *   entropy_out   [n_tokens] fp32, may be NULL
+ *   workspace     rlk_workspace_bytes(RLK_OP_FROM_LOGITS, ...) bytes (may be NULL if 0)
+ * Sizes: 1 <= vocab < 2^31, 0 <= n_tokens < 2^31.
+ */
+rlk_status rlk_logprob_from_logits(const float* logits, int64_t ld_logits, int64_t n_tokens,
+                                   int64_t vocab, const int64_t* target_ids, float temperature,
+                                   int32_t vocab_splits, float* logprob_out, float* entropy_out,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * LM-head projection fused with the selected-token logprob ("linear-logp"):
+ * logits = hidden * weight^T are formed tile by tile in fp32 (bf16 x bf16 products,
+ * fp32 accumulation in a fixed order over the hidden dimension, no split over it) and
+ * never written to memory.
+ *   hidden_bf16   [n_tokens, ld_hidden] bf16 bits, first hidden_dim columns used
+ *   weight_bf16   [vocab, ld_weight] bf16 bits (nn.Linear / lm_head layout)
+ *   hidden_dim    a positive multiple of 64, at most 2^20; ld_hidden, ld_weight >=
+ *                 hidden_dim, multiples of 8 and at most 2^22; both base pointers
+ *                 16-byte aligned; vocab at most 2^26
+ *   other arguments as rlk_logprob_from_logits; entropy_out may be NULL
+ */
+rlk_status rlk_linear_logprob(const uint16_t* hidden_bf16, int64_t ld_hidden,
+                              const uint16_t* weight_bf16, int64_t ld_weight, int64_t n_tokens,
+                              int64_t hidden_dim, int64_t vocab, const int64_t* target_ids,
+                              float temperature, int32_t vocab_splits, float* logprob_out,
+                              float* entropy_out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * Per-token entropy only (no targets).  Bitwise equal to the entropy output of
+ * rlk_logprob_from_logits with the same logits, temperature and any split count.
+ */
+rlk_status rlk_entropy(const float* logits, int64_t ld_logits, int64_t n_tokens, int64_t vocab,
+                       float temperature, int32_t vocab_splits, float* entropy_out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* rlk_status_string(rlk_status status);
+
+/* Static identifier of the implementation that runs (recorded next to results). */
+const char* rlk_backend_id(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLK_LOGPROB_H */

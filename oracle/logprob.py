@@ -75,14 +75,21 @@ def _rows_lse_entropy(z: np.ndarray):
     return L, H, bad
 
 
+def _row_block(n_cols: int) -> int:
+    """Rows per block so that one float64 temporary stays near 2M elements (small enough
+    for the allocator to reuse; the result does not depend on it: rows are independent)."""
+    return max(1, min(256, (1 << 21) // max(1, n_cols)))
+
+
 def logprob_entropy(x: np.ndarray, targets: np.ndarray | None, temperature: float = 1.0,
-                    block: int = 256):
+                    block: int | None = None):
     """Selected-token logprob and entropy of softmax(x / tau), row by row, in float64.
 
     x: [T, V] (any real dtype); targets: [T] integer ids or None.
     Returns (logprob[T] or None, entropy[T]) as float64 arrays."""
     x = np.asarray(x)
     T, V = x.shape
+    block = block or _row_block(V)
     lp = None if targets is None else np.empty(T, dtype=np.float64)
     H = np.empty(T, dtype=np.float64)
     for r0 in range(0, T, block):
@@ -113,7 +120,7 @@ def linear_logits(h: np.ndarray, w: np.ndarray) -> np.ndarray:
 
 
 def linear_logprob_entropy(h: np.ndarray, w: np.ndarray, targets: np.ndarray | None,
-                           temperature: float = 1.0, block: int = 128):
+                           temperature: float = 1.0, block: int | None = None):
     """Logprob and entropy of softmax((H W^T)/tau) per row; the LM-head projection of the
     strict linear-logp operator followed by the same definition as logprob_entropy."""
     h = np.asarray(h)
@@ -121,11 +128,11 @@ def linear_logprob_entropy(h: np.ndarray, w: np.ndarray, targets: np.ndarray | N
     lp = None if targets is None else np.empty(T, dtype=np.float64)
     H = np.empty(T, dtype=np.float64)
     w64 = np.asarray(w, dtype=np.float64)
+    block = block or _row_block(w64.shape[0])
     for r0 in range(0, T, block):
         r1 = min(T, r0 + block)
         x = linear_logits(h[r0:r1], w64)
-        a, b = logprob_entropy(x, None if targets is None else targets[r0:r1],
-                               temperature, block=r1 - r0)
+        a, b = logprob_entropy(x, None if targets is None else targets[r0:r1], temperature)
         H[r0:r1] = b
         if lp is not None:
             lp[r0:r1] = a

@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol, sizes
+workspaces on the host, and rejects bad arguments before touching any device.
+
+Pointers passed here are never dereferenced: validation is host-only and returns before
+anything is launched.  The one test that reaches the device check (valid arguments on a
+machine without a gfx950 GPU) is skipped wherever a GPU is visible, since there it would
+launch kernels on those placeholder pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import pytest
+
+from entropy_rlk_logprob_amd import binding as B
+
+FAKE = 0x10000  # placeholder device address (never dereferenced on these paths)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return B.load()
+
+
+def no_gpu_visible() -> bool:
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+def test_exports_every_header_symbol(L):
+    names = B.header_functions()
+    assert set(names) == {"rlk_workspace_bytes", "rlk_logprob_from_logits", "rlk_linear_logprob",
+                          "rlk_entropy", "rlk_status_string", "rlk_backend_id"}
+    for n in names:
+        assert hasattr(L.lib, n), n
+        assert ctypes.cast(getattr(L.lib, n), ctypes.c_void_p).value
+
+
+def test_backend_and_status_strings(L):
+    assert L.backend_id() == "rlk.logprob.strict.gfx950.v1"
+    for st in range(5):
+        assert L.status_string(st)
+    assert L.status_string(99) == "unknown status"
+
+
+def test_workspace_sizes(L):
+    assert L.workspace_bytes(B.OP_FROM_LOGITS, 1024, 151936, 0, 1) == 0
+    assert L.workspace_bytes(B.OP_FROM_LOGITS, 1024, 151936, 0, 4) == 4 * 1024 * 24
+    assert L.workspace_bytes(B.OP_ENTROPY, 1024, 151936, 0, 8) == 8 * 1024 * 24
+    # fused: 8 chunks x ceil(18992 / 256) = 600 tile states per token, + target logits
+    lin = L.workspace_bytes(B.OP_LINEAR, 1024, 151936, 2048, 1)
+    assert lin == 600 * 1024 * 24 + 4096
+    lin4 = L.workspace_bytes(B.OP_LINEAR, 1024, 151936, 2048, 4)
+    assert lin4 == lin + 4 * 1024 * 24
+    assert L.workspace_bytes(B.OP_LINEAR, 0, 151936, 2048, 1) == 0
+    out = ctypes.c_size_t()
+    assert L.lib.rlk_workspace_bytes(7, 1, 1, 0, 1, ctypes.byref(out)) == B.RLK_ERR_INVALID_ARGUMENT
+    assert L.lib.rlk_workspace_bytes(0, 1, 1, 0, 3, ctypes.byref(out)) == B.RLK_ERR_INVALID_ARGUMENT
+    assert L.lib.rlk_workspace_bytes(0, -1, 1, 0, 1, ctypes.byref(out)) == B.RLK_ERR_INVALID_ARGUMENT
+    assert L.lib.rlk_workspace_bytes(0, 1, 0, 0, 1, ctypes.byref(out)) == B.RLK_ERR_INVALID_ARGUMENT
+    assert L.lib.rlk_workspace_bytes(0, 1, 1, 0, 1, None) == B.RLK_ERR_INVALID_ARGUMENT
+
+
+def call_logits(L, logits=FAKE, ld=1024, T=4, V=1024, targets=FAKE, tau=1.0, S=1, lp=FAKE,
+                ent=FAKE, ws=None, wsb=0):
+    return L.logprob_from_logits_raw(logits, ld, T, V, targets, tau, S, lp, ent, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=None), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(targets=None), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(lp=None), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(T=-1), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(V=0), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(ld=1000), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(tau=0.0), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(tau=-1.0), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(tau=math.inf), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(tau=math.nan), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(S=3), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(S=16), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(S=0), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(S=4), B.RLK_ERR_WORKSPACE_TOO_SMALL),
+    (dict(S=4, ws=FAKE, wsb=4 * 4 * 24 - 1), B.RLK_ERR_WORKSPACE_TOO_SMALL),
+    (dict(S=4, ws=FAKE + 8, wsb=4 * 4 * 24), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(T=0, logits=None, targets=None, lp=None), B.RLK_OK),
+])
+def test_logits_validation(L, kw, code):
+    assert call_logits(L, **kw) == code
+
+
+def test_entropy_validation(L):
+    e = L.entropy_raw
+    assert e(FAKE, 1024, 4, 1024, 1.0, 1, None, None, 0, None) == B.RLK_ERR_INVALID_ARGUMENT
+    assert e(FAKE, 1024, 4, 1024, 1.0, 5, FAKE, None, 0, None) == B.RLK_ERR_INVALID_ARGUMENT
+    assert e(FAKE, 1024, 4, 1024, 1.0, 2, FAKE, None, 0, None) == B.RLK_ERR_WORKSPACE_TOO_SMALL
+    assert e(None, 1024, 0, 1024, 1.0, 1, None, None, 0, None) == B.RLK_OK
+
+
+def call_linear(L, h=FAKE, ldh=2048, w=FAKE, ldw=2048, T=4, d=2048, V=1000, tg=FAKE, tau=1.0,
+                S=1, lp=FAKE, ent=None, ws=FAKE, wsb=1 << 30):
+    return L.linear_logprob_raw(h, ldh, w, ldw, T, d, V, tg, tau, S, lp, ent, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(h=None), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(w=None), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(tg=None), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(d=100, ldh=100, ldw=100), B.RLK_ERR_INVALID_ARGUMENT),   # not a multiple of 64
+    (dict(d=0), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(ldh=2040), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(ldw=2052), B.RLK_ERR_INVALID_ARGUMENT),                   # not a multiple of 8
+    (dict(ldw=(1 << 22) + 8), B.RLK_ERR_INVALID_ARGUMENT),           # stride too large
+    (dict(V=(1 << 26) + 1), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(h=FAKE + 2), B.RLK_ERR_INVALID_ARGUMENT),                 # not 16-byte aligned
+    (dict(tau=0.0), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(S=6), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(V=0), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(ws=None), B.RLK_ERR_WORKSPACE_TOO_SMALL),
+    (dict(wsb=100), B.RLK_ERR_WORKSPACE_TOO_SMALL),
+    (dict(ws=FAKE + 64), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(T=0, h=None, w=None, tg=None, lp=None, ws=None, wsb=0), B.RLK_OK),
+])
+def test_linear_validation(L, kw, code):
+    assert call_linear(L, **kw) == code
+
+
+@pytest.mark.skipif(not no_gpu_visible(), reason="would launch on placeholder pointers")
+def test_valid_call_without_gfx950_is_unsupported_device(L):
+    assert call_logits(L) == B.RLK_ERR_UNSUPPORTED_DEVICE
+    assert call_linear(L) == B.RLK_ERR_UNSUPPORTED_DEVICE
+    assert L.entropy_raw(FAKE, 1024, 4, 1024, 1.0, 1, FAKE, None, 0, None) == \
+        B.RLK_ERR_UNSUPPORTED_DEVICE

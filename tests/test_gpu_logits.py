@@ -1,0 +1,208 @@
+"""GPU parity of the logits path (rlk_logprob_from_logits, rlk_entropy) against the fp64
+oracle, and the strictness properties: bitwise invariance to vocab split, batch
+composition, row order and repeats, plus closed forms and non-finite rows."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from entropy_rlk_logprob_amd import synthetic as S
+from tests.helpers import (TOL_LOGITS, announce, bitwise_equal, dev, max_abs, run_logits)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cfg2():
+    announce("generating logits workload T=1024 V=151936 (seed 1002)")
+    case = S.logits_workload(2)
+    lp, ent = oracle.logprob_entropy(case.x, case.targets, case.temperature)
+    return case, lp, ent, dev(case.x), dev(case.targets)
+
+
+@pytest.mark.parametrize("split", [1, 4])
+def test_tiny_workload_vs_oracle(lib, split):
+    case = S.logits_workload(1)
+    announce(f"logits T=64 V=1024 split={split}")
+    lp, ent = run_logits(lib, case.x, case.targets, 1.0, split)
+    olp, oent = oracle.logprob_entropy(case.x, case.targets)
+    assert max_abs(lp, olp) <= TOL_LOGITS
+    assert max_abs(ent, oent) <= TOL_LOGITS
+
+
+def test_tiny_workload_split_bitwise(lib):
+    case = S.logits_workload(1)
+    ref = run_logits(lib, case.x, case.targets, 1.0, 1)
+    for split in (2, 4, 8):
+        announce(f"logits T=64 V=1024 split {split} vs 1")
+        got = run_logits(lib, case.x, case.targets, 1.0, split)
+        assert bitwise_equal(got[0], ref[0]) and bitwise_equal(got[1], ref[1]), split
+
+
+@pytest.mark.parametrize("T,V,tau", [
+    (1, 1, 1.0), (3, 2, 1.0), (5, 3, 0.7), (7, 7, 1.0), (4, 100, 0.7), (9, 1000, 1.0),
+    (6, 1023, 1.0), (3, 4097, 2.0), (33, 20000, 0.7), (2, 65536 + 17, 1.0),
+    (5, 257 * 8 + 3, 1.0), (17, 151936, 0.7),
+])
+def test_shapes_vs_oracle(lib, T, V, tau):
+    """Several tiles per lane and ragged tails (V not a multiple of 4, 8, 64 or 256)."""
+    announce(f"logits T={T} V={V} tau={tau}")
+    case = S.random_logits_case(T, V, 3.0, seed=7000 + V)
+    olp, oent = oracle.logprob_entropy(case.x, case.targets, tau)
+    ref = None
+    for split in (1, 2, 4, 8):
+        lp, ent = run_logits(lib, case.x, case.targets, tau, split)
+        assert max_abs(lp, olp) <= TOL_LOGITS, (split, max_abs(lp, olp))
+        assert max_abs(ent, oent) <= TOL_LOGITS, (split, max_abs(ent, oent))
+        if ref is None:
+            ref = (lp, ent)
+        else:
+            assert bitwise_equal(lp, ref[0]) and bitwise_equal(ent, ref[1]), split
+
+
+def test_strided_and_unaligned_rows_bitwise(lib):
+    """Row stride > V (padded rows) and a base that is not 16-byte aligned (element loads
+    instead of 16-byte loads) give the same bits as the dense aligned call."""
+    import torch
+    T, V = 12, 5003
+    case = S.random_logits_case(T, V, 2.0, seed=71)
+    ref = run_logits(lib, case.x, case.targets)
+    big = np.full((T, V + 13), np.nan, dtype=np.float32)
+    big[:, 1:V + 1] = case.x
+    bd = dev(big)
+    announce("logits strided unaligned view")
+    view = bd[:, 1:V + 1]
+    assert view.data_ptr() % 16 != 0 and view.stride(0) == V + 13
+    got = run_logits(lib, view, case.targets)
+    assert bitwise_equal(got[0], ref[0]) and bitwise_equal(got[1], ref[1])
+    big2 = np.full((T, V + 3), np.nan, dtype=np.float32)
+    big2[:, :V] = case.x
+    got2 = run_logits(lib, dev(big2)[:, :V], case.targets)
+    assert bitwise_equal(got2[0], ref[0]) and bitwise_equal(got2[1], ref[1])
+    del torch
+
+
+def test_qwen3_vocab_workload_vs_oracle(lib, cfg2):
+    case, olp, oent, xd, td = cfg2
+    announce("logits T=1024 V=151936 split=1 vs oracle")
+    lp, ent = run_logits(lib, xd, td, 1.0, 1)
+    e_lp, e_ent = max_abs(lp, olp), max_abs(ent, oent)
+    print(f"max_abs_vs_fp64 logprob={e_lp:.3e} entropy={e_ent:.3e}")
+    assert e_lp <= TOL_LOGITS and e_ent <= TOL_LOGITS
+    # spiked rows: their sampled targets are almost surely the spike -> logprob near 0
+    sp = case.spiked_rows
+    assert np.all(np.abs(lp[sp] - olp[sp]) <= TOL_LOGITS)
+
+
+def test_qwen3_vocab_split_bitwise(lib, cfg2):
+    _, _, _, xd, td = cfg2
+    ref = run_logits(lib, xd, td, 1.0, 1)
+    for split in (2, 4, 8):
+        announce(f"logits T=1024 V=151936 split={split} vs 1")
+        got = run_logits(lib, xd, td, 1.0, split)
+        assert bitwise_equal(got[0], ref[0]) and bitwise_equal(got[1], ref[1]), split
+
+
+def test_qwen3_vocab_batch_and_order_bitwise(lib, cfg2):
+    """Any subset or permutation of rows gives the same bits per row."""
+    case, _, _, xd, td = cfg2
+    ref_lp, ref_ent = run_logits(lib, xd, td)
+    for perm in S.permutations(2, 1024, 2):
+        announce("logits T=1024 row permutation")
+        lp, ent = run_logits(lib, xd[perm], td[perm])
+        assert bitwise_equal(lp, ref_lp[perm]) and bitwise_equal(ent, ref_ent[perm])
+    for lo, hi in [(0, 1), (5, 12), (1000, 1024), (3, 515)]:
+        announce(f"logits rows [{lo},{hi}) alone")
+        lp, ent = run_logits(lib, xd[lo:hi], td[lo:hi], 1.0, 4)
+        assert bitwise_equal(lp, ref_lp[lo:hi]) and bitwise_equal(ent, ref_ent[lo:hi])
+
+
+def test_repeats_one_distinct_result(lib, cfg2):
+    _, _, _, xd, td = cfg2
+    announce("logits T=1024 10 repeats")
+    outs = {run_logits(lib, xd, td)[0].tobytes() + run_logits(lib, xd, td)[1].tobytes()
+            for _ in range(5)}
+    assert len(outs) == 1
+
+
+def test_entropy_call_matches_entropy_output(lib, cfg2):
+    import torch
+    _, _, _, xd, td = cfg2
+    _, ref_ent = run_logits(lib, xd, td, 1.0, 1)
+    for split in (1, 8):
+        announce(f"rlk_entropy T=1024 split={split}")
+        ent = lib.entropy(xd, 1.0, split)
+        torch.cuda.synchronize()
+        assert bitwise_equal(ent.cpu().numpy(), ref_ent)
+
+
+def test_closed_forms(lib):
+    announce("logits closed forms")
+    for V in (1, 2, 1024, 151936):
+        x = np.full((3, V), 1.5, dtype=np.float32)
+        t = np.array([0, V - 1, V // 2])
+        lp, ent = run_logits(lib, x, t)
+        assert np.all(np.abs(lp + math.log(V)) <= TOL_LOGITS), (V, lp)
+        assert np.all(np.abs(ent - math.log(V)) <= TOL_LOGITS), (V, ent)
+    lp, ent = run_logits(lib, np.array([[3.25]], np.float32), np.array([0]))
+    assert lp[0] == 0.0 and ent[0] == 0.0
+    x = np.zeros((1, 4096), np.float32)
+    x[0, 77] = 100.0
+    lp, ent = run_logits(lib, x, np.array([77]))
+    assert -1e-30 <= lp[0] <= 0.0 and 0.0 <= ent[0] < 1e-30
+
+
+def test_shift_and_temperature_bitwise(lib):
+    """On grid-valued logits every difference is exact: a shift by 64 and a power-of-two
+    temperature (tau = 2 vs logits halved) give identical bits."""
+    x = S.grid_logits(40, 30011, seed=9)
+    t = np.random.default_rng(9).integers(0, 30011, size=40)
+    announce("logits shift/temperature invariance")
+    a = run_logits(lib, x, t)
+    b = run_logits(lib, x + np.float32(64.0), t)
+    assert bitwise_equal(a[0], b[0]) and bitwise_equal(a[1], b[1])
+    c = run_logits(lib, x, t, 2.0)
+    d = run_logits(lib, x / np.float32(2.0), t, 1.0)
+    assert bitwise_equal(c[0], d[0]) and bitwise_equal(c[1], d[1])
+
+
+def test_nonfinite_rows_and_targets(lib):
+    rng = np.random.default_rng(3)
+    T, V = 8, 3000
+    x = rng.normal(0, 2, size=(T, V)).astype(np.float32)
+    x[0, 5] = np.nan
+    x[1, 2999] = np.inf
+    x[2, :] = -np.inf
+    x[3, 1000:] = -np.inf
+    x[4, :2999] = -np.inf         # one finite token: logprob 0, entropy 0
+    t = np.array([1, 1, 1, 1500, 2999, -1, V, 7])
+    announce("logits non-finite rows")
+    olp, oent = oracle.logprob_entropy(x, t)
+    for split in (1, 2, 8):
+        lp, ent = run_logits(lib, x, t, 1.0, split)
+        assert np.isnan(lp[0]) and np.isnan(ent[0])
+        assert np.isnan(lp[1]) and np.isnan(ent[1])
+        assert np.isnan(lp[2]) and np.isnan(ent[2])
+        assert np.isneginf(lp[3]) and abs(ent[3] - oent[3]) <= TOL_LOGITS
+        assert lp[4] == 0.0 and ent[4] == 0.0
+        assert np.isnan(lp[5]) and np.isnan(lp[6])
+        assert max_abs(ent[5:], oent[5:]) <= TOL_LOGITS
+        assert abs(lp[7] - olp[7]) <= TOL_LOGITS
+    # -inf masking equals the smaller vocabulary (within tolerance: different chunking)
+    xm = x[3:4, :1000]
+    lps, ents = run_logits(lib, xm, np.array([5]))
+    lpm, entm = run_logits(lib, x[3:4], np.array([5]))
+    assert abs(lps[0] - lpm[0]) <= TOL_LOGITS and abs(ents[0] - entm[0]) <= TOL_LOGITS
+
+
+def test_empty_batch(lib):
+    import torch
+    announce("logits T=0")
+    x = torch.empty((0, 100), dtype=torch.float32, device="cuda")
+    t = torch.empty((0,), dtype=torch.int64, device="cuda")
+    lp, ent = lib.logprob_from_logits(x, t)
+    torch.cuda.synchronize()
+    assert lp.numel() == 0 and ent.numel() == 0
