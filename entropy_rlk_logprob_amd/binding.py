@@ -52,6 +52,10 @@ class Library:
                 f"{path} is not built; run `python -m entropy_rlk_logprob_amd.build` "
                 "(there is no fallback implementation)")
         self.path = path
+        # torch ships its own HIP runtime under the same soname (libamdhip64.so.7); load it
+        # first so this library binds to that one instance instead of pulling in a second
+        # HIP runtime (with its own device state) from the system ROCm.
+        import torch  # noqa: F401
         self.lib = ctypes.CDLL(path)
         L = self.lib
         L.rlk_workspace_bytes.restype = ctypes.c_int

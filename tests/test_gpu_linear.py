@@ -1,0 +1,148 @@
+"""GPU parity of the fused linear-logp path (rlk_linear_logprob) against the fp64 oracle
+(logits as exact float64 dot products of the bf16 values), and its strictness: bitwise
+invariance to vocab split, to packing (each sequence alone vs the packed batch), to row
+permutations and to repeats."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from entropy_rlk_logprob_amd import synthetic as S
+from tests.helpers import TOL_LINEAR, announce, bits_dev, bitwise_equal, dev, max_abs, run_linear
+
+pytestmark = pytest.mark.gpu
+
+
+def f32(bits):
+    return S.bf16_bits_to_f32(bits)
+
+
+def oracle_rows(case, rows, targets=None, tau=None):
+    tau = case.temperature if tau is None else tau
+    t = (case.targets if targets is None else targets)[rows]
+    return oracle.linear_logprob_entropy(f32(case.h_bits[rows]), f32(case.w_bits), t, tau)
+
+
+@pytest.mark.parametrize("T,d,V,tau", [
+    (1, 64, 1, 1.0), (3, 64, 100, 1.0), (37, 128, 1000, 0.7), (257, 192, 5003, 1.0),
+    (300, 256, 20000, 0.7), (513, 64, 2049, 1.0), (64, 512, 151936, 1.0),
+])
+def test_shapes_vs_oracle_and_split_bitwise(lib, T, d, V, tau):
+    """Several token and vocab tiles with ragged tails; logits of spread ~3 so that a
+    wrong row, column or k-block shows up far above the tolerance."""
+    announce(f"linear T={T} d={d} V={V} tau={tau}")
+    case = S.random_fused_case(T, d, V, seed=9000 + T + V, h_sigma=1.0,
+                               w_sigma=3.0 / math.sqrt(d), temperature=tau)
+    olp, oent = oracle.linear_logprob_entropy(f32(case.h_bits), f32(case.w_bits), case.targets,
+                                              tau)
+    h, w, t = bits_dev(case.h_bits), bits_dev(case.w_bits), dev(case.targets)
+    ref = None
+    for split in (1, 2, 4, 8):
+        lp, ent = run_linear(lib, h, w, t, tau, split)
+        assert max_abs(lp, olp) <= TOL_LINEAR, (split, max_abs(lp, olp))
+        assert max_abs(ent, oent) <= TOL_LINEAR, (split, max_abs(ent, oent))
+        if ref is None:
+            ref = (lp, ent)
+        else:
+            assert bitwise_equal(lp, ref[0]) and bitwise_equal(ent, ref[1]), split
+
+
+def test_uniform_when_weight_is_zero(lib):
+    announce("linear zero weight -> uniform")
+    T, d, V = 5, 128, 3000
+    h = S.to_bf16_bits(np.ones((T, d), np.float32))
+    w = np.zeros((V, d), np.uint16)
+    lp, ent = run_linear(lib, h, w, np.array([0, 1, 2999, 1500, 7]))
+    assert np.all(np.abs(lp + math.log(V)) <= 1e-6) and np.all(np.abs(ent - math.log(V)) <= 1e-6)
+
+
+def test_out_of_range_targets_and_empty(lib):
+    import torch
+    case = S.random_fused_case(6, 64, 700, seed=3, w_sigma=0.3)
+    t = case.targets.copy()
+    t[1] = -1
+    t[4] = 700
+    announce("linear out-of-range targets")
+    lp, ent = run_linear(lib, case.h_bits, case.w_bits, t)
+    olp, oent = oracle.linear_logprob_entropy(f32(case.h_bits), f32(case.w_bits), t)
+    assert np.isnan(lp[1]) and np.isnan(lp[4])
+    assert max_abs(lp, olp) <= TOL_LINEAR and max_abs(ent, oent) <= TOL_LINEAR
+    hd = torch.empty((0, 64), dtype=torch.int16, device="cuda")
+    lp0, ent0 = lib.linear_logprob(hd, bits_dev(case.w_bits), dev(np.zeros(0, np.int64)))
+    torch.cuda.synchronize()
+    assert lp0.numel() == 0 and ent0.numel() == 0
+
+
+@pytest.fixture(scope="module")
+def cfg3():
+    announce("generating fused workload T=1024 d=2048 V=151936")
+    c = S.fused_workload(3)
+    return c, bits_dev(c.h_bits), bits_dev(c.w_bits), dev(c.targets)
+
+
+def test_qwen3next_shape_sampled_rows_vs_oracle(lib, cfg3):
+    case, h, w, t = cfg3
+    announce("linear T=1024 d=2048 V=151936 vs oracle (sampled rows)")
+    lp, ent = run_linear(lib, h, w, t)
+    rows = np.unique(np.concatenate([np.arange(0, 1024, 37), [1, 255, 256, 511, 1023]]))
+    olp, oent = oracle_rows(case, rows)
+    e1, e2 = max_abs(lp[rows], olp), max_abs(ent[rows], oent)
+    print(f"max_abs_vs_fp64 logprob={e1:.3e} entropy={e2:.3e} over {len(rows)} rows")
+    assert e1 <= TOL_LINEAR and e2 <= TOL_LINEAR
+    for split in (2, 4, 8):
+        announce(f"linear T=1024 split={split} vs 1")
+        lps, ents = run_linear(lib, h, w, t, 1.0, split)
+        assert bitwise_equal(lps, lp) and bitwise_equal(ents, ent), split
+    outs = {b"".join(x.tobytes() for x in run_linear(lib, h, w, t)) for _ in range(4)}
+    assert len(outs) == 1
+
+
+def test_qwen3_8b_shape_sequences_alone_bitwise(lib):
+    """16 packed sequences of 128 rows: each sequence alone gives the packed bits."""
+    announce("generating fused workload T=2048 d=4096 V=151936")
+    case = S.fused_workload(4)
+    h, w, t = bits_dev(case.h_bits), bits_dev(case.w_bits), dev(case.targets)
+    announce("linear T=2048 d=4096 packed")
+    lp, ent = run_linear(lib, h, w, t)
+    starts = np.concatenate([[0], np.cumsum(case.seq_lens)])
+    for i in range(len(case.seq_lens)):
+        a, b = int(starts[i]), int(starts[i + 1])
+        announce(f"linear sequence {i} rows [{a},{b}) alone")
+        lps, ents = run_linear(lib, h[a:b], w, t[a:b])
+        assert bitwise_equal(lps, lp[a:b]) and bitwise_equal(ents, ent[a:b]), i
+    rows = np.array([0, 127, 128, 1000, 1500, 2047])
+    olp, oent = oracle_rows(case, rows)
+    assert max_abs(lp[rows], olp) <= TOL_LINEAR and max_abs(ent[rows], oent) <= TOL_LINEAR
+
+
+def test_large_ragged_batch_permutations_and_split(lib):
+    """T = 16384 (ragged sequences up to 4096), d = 4096, tau = 0.7: sampled rows against
+    the oracle with targets drawn from the oracle's tempered softmax; bitwise identical
+    across three row permutations and vocab splits 1 and 4."""
+    import torch
+    announce("generating fused workload T=16384 d=4096 V=151936 tau=0.7")
+    case = S.fused_workload(5)
+    T = case.h_bits.shape[0]
+    rng = np.random.default_rng(5005)
+    rows = np.sort(rng.choice(T, size=24, replace=False))
+    targets = S.uniform_targets(rng, T, case.w_bits.shape[0])
+    z = oracle.linear_logits(f32(case.h_bits[rows]), f32(case.w_bits)) / float(np.float32(0.7))
+    targets[rows] = oracle.sample_targets(z, S.target_uniforms(5, len(rows)))
+    h, w, t = bits_dev(case.h_bits), bits_dev(case.w_bits), dev(targets)
+    announce("linear T=16384 split=1")
+    lp, ent = run_linear(lib, h, w, t, 0.7, 1)
+    olp, oent = oracle_rows(case, rows, targets, 0.7)
+    e1, e2 = max_abs(lp[rows], olp), max_abs(ent[rows], oent)
+    print(f"max_abs_vs_fp64 logprob={e1:.3e} entropy={e2:.3e}")
+    assert e1 <= TOL_LINEAR and e2 <= TOL_LINEAR
+    announce("linear T=16384 split=4")
+    lp4, ent4 = run_linear(lib, h, w, t, 0.7, 4)
+    assert bitwise_equal(lp4, lp) and bitwise_equal(ent4, ent)
+    for k, perm in enumerate(S.permutations(5, T, 3)):
+        announce(f"linear T=16384 permutation {k}")
+        pd = torch.from_numpy(perm).cuda()
+        lpp, entp = run_linear(lib, h[pd].contiguous(), w, t[pd].contiguous(), 0.7, 1)
+        assert bitwise_equal(lpp, lp[perm]) and bitwise_equal(entp, ent[perm]), k
