@@ -19,7 +19,7 @@
 // Workgroup: 8 waves, a 256 (vocab) x 256 (token) output tile, waves arranged 2 (vocab)
 // x 4 (token), each wave 128 x 64 = 4 x 2 MFMA blocks.  K step 64 with two LDS stages
 // (64 KiB each: the W and H slices with an XOR swizzle on 16-byte columns so that
-// ds_read_b128 of 8 consecutive rows hits distinct banks).  Workgroup ids are remapped
+// ds_read_b128 of 16 consecutive rows hits distinct banks).  Workgroup ids are remapped
 // so that the token tiles of one vocabulary tile run back to back on the same XCD and
 // share its W slice in that XCD's L2.
 
@@ -45,12 +45,20 @@ struct alignas(16) U4 {
   uint32_t x, y, z, w;
 };
 
-// Byte offset of 16-byte column `c16` (0..7) of tile row `row` in a [rows][64] bf16 slab.
-__device__ __forceinline__ int swz(int row, int c16) { return row * 128 + ((c16 ^ (row & 7)) << 4); }
+// All LDS-DMA loads of this wave have landed.
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ bf16x8 lds_frag(const char* base, int row, int c16) {
-  const U4 v = *reinterpret_cast<const U4*>(base + swz(row, c16));
-  return __builtin_bit_cast(bf16x8, v);
+// Workgroup barrier ordering LDS reads (this wave's ds_reads done, then s_barrier).  The
+// LDS-DMA stage that the next step reads was waited for by every wave before it arrives.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// LDS slab layout: rows of kBK bf16 = 128 bytes; 16-byte column c16 of row r sits at
+// physical column c16 ^ ((r / 2) % 8).  The XOR key makes the 16 rows that one 16-lane
+// ds_read_b128 pass touches land in 16 distinct 16-byte bank groups of the 64-bank LDS.
+__device__ __forceinline__ int lds_offset(int row, int c16) {
+  return row * 128 + ((c16 ^ ((row >> 1) & 7)) << 4);
 }
 
 struct TileGeom {
@@ -99,36 +107,37 @@ __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
   const int wt = wave & 3;   // token quarter (0..3)
 
   // Global -> LDS: direct 16-byte-per-lane loads into LDS (global_load_lds_dwordx4).  One
-  // wave instruction fills one 1 KiB block = 8 slab rows; lane l writes physical column
-  // l % 8 of row l / 8 in the block, so it fetches logical column (l % 8) ^ (l / 8) --
-  // the XOR swizzle is applied on the source side.  Wave w fills blocks 4 w .. 4 w + 3
-  // of both slabs.  Offsets are tile-relative on workgroup-uniform bases; rows beyond
-  // the valid range are clamped to the last valid row (masked later, never stored).
+  // wave instruction fills one 1 KiB block = 8 slab rows: lane l writes physical column
+  // l % 8 of row r = 8 b + l / 8 of block b, so it fetches logical column
+  // (l % 8) ^ ((r / 2) % 8), the layout of lds_offset().  Blocks 0..31 are the W slab,
+  // 32..63 the H slab; wave w fills blocks w, w + 8, ..., w + 56.  Offsets are
+  // tile-relative on workgroup-uniform bases; rows beyond the valid range are clamped to
+  // the last valid row (their values are masked in the epilogue or never stored).
+  constexpr int kBlocksPerWave = (kTileV + kTileT) / 8 / (kThreads / 64);  // 8
+  constexpr int kWBlocks = kTileV / 8;
   const uint16_t* __restrict__ Wt = W + v_lo * ldw;
   const uint16_t* __restrict__ Ht = H + t_lo * ldh;
   const int w_last = (int)min(g.V - 1 - v_lo, (int64_t)(kTileV - 1));
   const int h_last = (int)min(g.T - 1 - t_lo, (int64_t)(kTileT - 1));
-  const int src_c16 = (lane & 7) ^ (lane >> 3);
-  int woff[4], hoff[4];
+  int src_off[kBlocksPerWave];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (wave * 4 + i) * 8 + (lane >> 3);
-    woff[i] = min(row, w_last) * (int)ldw + src_c16 * 8;
-    hoff[i] = min(row, h_last) * (int)ldh + src_c16 * 8;
+  for (int i = 0; i < kBlocksPerWave; ++i) {
+    const int blk = i * 8 + wave;
+    const bool is_w = i < kWBlocks / 8;
+    const int bb = is_w ? blk : blk - kWBlocks;
+    const int row = bb * 8 + (lane >> 3);
+    const int col = ((lane & 7) ^ ((row >> 1) & 7)) * 8;
+    src_off[i] = is_w ? (min(row, w_last) * (int)ldw + col) : (min(row, h_last) * (int)ldh + col);
   }
   auto issue_stage = [&](int64_t k0, int stage) {
-    char* wb = smem + stage * kStageBytes + wave * 4 * 1024;
-    char* hb = smem + stage * kStageBytes + kTileV * kBK * 2 + wave * 4 * 1024;
-    const uint16_t* wk = Wt + k0;
-    const uint16_t* hk = Ht + k0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(wk + woff[i]),
-                                       (__attribute__((address_space(3))) void*)(wb + i * 1024),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(hk + hoff[i]),
-                                       (__attribute__((address_space(3))) void*)(hb + i * 1024),
-                                       16, 0, 0);
+    for (int i = 0; i < kBlocksPerWave; ++i) {
+      const int blk = i * 8 + wave;
+      const bool is_w = i < kWBlocks / 8;
+      const uint16_t* src = (is_w ? Wt : Ht) + k0 + src_off[i];
+      char* dst = smem + stage * kStageBytes + blk * 1024;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
   };
 
@@ -141,33 +150,43 @@ __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
   const int nk = (int)(d / kBK);
-  issue_stage(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
   const int frow = lane & 31;
   const int fhalf = lane >> 5;
+  issue_stage(0, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    // The other stage was last read in iteration kt - 1, which every wave has left.
+    // Stage kt has landed for every wave, and every wave is done reading stage kt - 1,
+    // whose buffer the loads of stage kt + 1 now overwrite.
+    wait_dma();
+    lds_barrier();
     if (kt + 1 < nk) issue_stage((int64_t)(kt + 1) * kBK, (kt + 1) & 1);
     const char* wb = smem + (kt & 1) * kStageBytes;
     const char* hb = wb + kTileV * kBK * 2;
+    // Fragments of step ks + 1 are read from LDS while the MFMAs of step ks run.
+    bf16x8 af[2][4], bfr[2][2];
+    auto read_frags = [&](int ks, int buf) {
+      const int c16 = 2 * ks + fhalf;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        af[buf][a] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const U4*>(wb + lds_offset(wv * 128 + a * 32 + frow, c16)));
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        bfr[buf][b] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const U4*>(hb + lds_offset(wt * 64 + b * 32 + frow, c16)));
+    };
+    read_frags(0, 0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int c16 = 2 * ks + fhalf;
-      bf16x8 af[4], bfr[2];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) af[a] = lds_frag(wb, wv * 128 + a * 32 + frow, c16);
-#pragma unroll
-      for (int b = 0; b < 2; ++b) bfr[b] = lds_frag(hb, wt * 64 + b * 32 + frow, c16);
+      if (ks + 1 < 4) read_frags(ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][a], bfr[ks & 1][b],
+                                                              acc[a][b], 0, 0, 0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
   }
+  __syncthreads();
 
   // ---------------------------------------------------------------- epilogue
   // Each lane owns tokens wt*64 + b*32 + (lane%32), b = 0, 1, and for each of them the
