@@ -101,6 +101,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run 5 device-to-device copies of the logits tensor (a plain copy of "
+                         "known size, used to calibrate the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -137,6 +140,13 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "kernel": "row_reduce_kernel<8,true>",
                 "kernel_ms": round(k_ms, 5), "algorithmic_bytes": alg_bytes}
+
+    if args.copy_probe:
+        dst = torch.empty_like(x)
+        for _ in range(5):
+            dst.copy_(x)
+        torch.cuda.synchronize()
+        del dst
 
     splits = {}
     for sp in (2, 4, 8):
