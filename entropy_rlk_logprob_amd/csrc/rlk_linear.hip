@@ -65,6 +65,7 @@ struct TileGeom {
   int64_t n_vt;       // vocabulary tiles (8 * tiles_per_chunk)
   int64_t n_tt;       // token tiles
   int64_t tpc;        // tiles per chunk
+  int64_t lane_tiles; // tiles per lane in the tile tree: max(1, next_pow2(tpc) / 64)
   int64_t Vc, V, T;
 };
 
@@ -200,17 +201,28 @@ __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
     // Target row relative to this tile, or -1 when the target is not in the tile.
     const int tloc = (tgt >= v_lo && tgt < v_hi) ? (int)(tgt - v_lo) : -1;
     State leaf[4];
+    float xt = 0.0f;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       float v[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int vr = wv * 128 + a * 32 + 8 * (i >> 2) + 4 * fhalf + (i & 3);
-        v[i] = (vr < n_valid) ? acc[a][b][i] : kNegInf;
-        if (vr == tloc) target_logit[tok] = acc[a][b][i];
+        v[i] = acc[a][b][i];
+        xt = (vr == tloc) ? v[i] : xt;
+      }
+      if (n_valid < kTileV) {  // workgroup-uniform: only the last tile of a chunk is short
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int vr = wv * 128 + a * 32 + 8 * (i >> 2) + 4 * fhalf + (i & 3);
+          v[i] = (vr < n_valid) ? v[i] : kNegInf;
+        }
       }
       leaf[a] = leaf16(v, c);
     }
+    // The one lane holding the target row of this token (if it lies in this tile) stores it.
+    if (tloc >= wv * 128 && tloc < wv * 128 + 128 && ((tloc >> 2) & 1) == fhalf)
+      target_logit[tok] = xt;
     State st = rlk_merge(rlk_merge(leaf[0], leaf[1], c), rlk_merge(leaf[2], leaf[3], c), c);
     const State o = shfl_xor_state(st, 32);
     half_state[b] = fhalf ? rlk_merge(o, st, c) : rlk_merge(st, o, c);
@@ -237,42 +249,54 @@ __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
   }
 }
 
-// Tiles of each chunk -> chunk states (balanced tree over tile index), chunks of a
-// shard -> shard state (tree8), then either the fp64 finalize (S = 1) or the shard's
-// wire state for the cross-shard merge.  Block: (256 / CPS) tokens x CPS chunks.
+// Tiles of each chunk -> chunk state, chunks of a shard -> shard state (tree8), then
+// either the fp64 finalize (S = 1) or the shard's wire state for the cross-shard merge.
+//
+// The tile tree is the perfect binary tree over tile index, padded with identity states
+// up to P = max(64, next power of two >= tiles per chunk) leaves (merging a state with the
+// identity on its right returns it unchanged, up to the sign of a zero u).  One wave per
+// (token, chunk): lane l first folds the aligned block of P / 64 tiles it owns (binary-
+// counter stack, identities elided), then an xor-butterfly over strides 1, 2, ..., 32
+// merges neighbouring blocks, lower lane first -- the upper levels of the same tree.
+// Block: CPS waves (the shard's chunks) for one token; grid (T, S).
 template <int CPS>
-__global__ __launch_bounds__(256) void tile_tree_kernel(
+__global__ __launch_bounds__(64 * CPS) void tile_tree_kernel(
     const WireState* __restrict__ tile_states, const float* __restrict__ target_logit,
     TileGeom g, const int64_t* __restrict__ targets, float c, double beta,
     float* __restrict__ lp_out, float* __restrict__ ent_out, WireState* __restrict__ shard_ws) {
-  constexpr int TPB = 256 / CPS;
-  const int j = threadIdx.x % TPB;
-  const int ci = threadIdx.x / TPB;
+  const int64_t tok = blockIdx.x;
   const int shard = blockIdx.y;
-  const int64_t tok = (int64_t)blockIdx.x * TPB + j;
+  const int ci = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int64_t chunk = (int64_t)shard * CPS + ci;
-  __shared__ State cs[CPS][TPB];
+  __shared__ State cs[CPS];
 
+  const WireState* __restrict__ base = tile_states + chunk * g.tpc * g.T + tok;
+  const int64_t k0 = (int64_t)lane * g.lane_tiles;
+  const int64_t k1 = min(k0 + g.lane_tiles, g.tpc);
   State r = identity_state();
-  if (tok < g.T) {
-    State stk[24];
+  if (g.lane_tiles == 1) {
+    if (k0 < k1) r = from_wire(base[k0 * g.T]);
+  } else if (k0 < k1) {
+    State stk[16];
     int top = 0;
-    const WireState* base = tile_states + chunk * g.tpc * g.T + tok;
-    for (int64_t k = 0; k < g.tpc; ++k) {
+    for (int64_t k = k0; k < k1; ++k) {
       State cur = from_wire(base[k * g.T]);
-      for (int64_t b = k; b & 1; b >>= 1) cur = rlk_merge(stk[--top], cur, c);
+      for (int64_t b = k - k0; b & 1; b >>= 1) cur = rlk_merge(stk[--top], cur, c);
       stk[top++] = cur;
     }
     r = stk[--top];
     while (top > 0) r = rlk_merge(stk[--top], r, c);
   }
-  cs[ci][j] = r;
-  __syncthreads();
-  if (ci != 0 || tok >= g.T) return;
-  State v[CPS];
 #pragma unroll
-  for (int i = 0; i < CPS; ++i) v[i] = cs[i][j];
-  const State root = tree8(v, CPS, c);
+  for (int off = 1; off < 64; off <<= 1) {
+    const State o = shfl_xor_state(r, off);
+    r = (lane & off) ? rlk_merge(o, r, c) : rlk_merge(r, o, c);
+  }
+  if (lane == 0) cs[ci] = r;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  const State root = tree8(cs, CPS, c);
   const int64_t t = targets ? targets[tok] : -1;
   if constexpr (CPS == 8) {
     const bool has = (t >= 0) && (t < g.V);
@@ -311,6 +335,9 @@ hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream) {
   const LinearWorkspace L = linear_workspace_layout(a.T, a.V, a.S);
   TileGeom g;
   g.tpc = L.tiles_per_chunk;
+  int64_t pow2 = 1;
+  while (pow2 < g.tpc) pow2 <<= 1;
+  g.lane_tiles = pow2 > 64 ? pow2 / 64 : 1;
   g.n_vt = L.n_tiles;
   g.n_tt = (a.T + kTileT - 1) / kTileT;
   g.Vc = a.Vc;
@@ -329,31 +356,24 @@ hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream) {
   const WireState* tiles = reinterpret_cast<const WireState*>(base + L.tile_states);
   const float* tl = reinterpret_cast<const float*>(base + L.target_logit);
   WireState* sws = reinterpret_cast<WireState*>(base + L.shard_states);
+  const dim3 tgrid((unsigned)a.T, (unsigned)a.S);
   switch (a.S) {
-    case 1: {
-      const dim3 grid((unsigned)((a.T + 31) / 32), 1);
-      hipLaunchKernelGGL((tile_tree_kernel<8>), grid, dim3(256), 0, stream, tiles, tl, g,
+    case 1:
+      hipLaunchKernelGGL((tile_tree_kernel<8>), tgrid, dim3(512), 0, stream, tiles, tl, g,
                          a.targets, a.c, a.beta, a.lp, a.ent, sws);
       return hipGetLastError();
-    }
-    case 2: {
-      const dim3 grid((unsigned)((a.T + 63) / 64), 2);
-      hipLaunchKernelGGL((tile_tree_kernel<4>), grid, dim3(256), 0, stream, tiles, tl, g,
+    case 2:
+      hipLaunchKernelGGL((tile_tree_kernel<4>), tgrid, dim3(256), 0, stream, tiles, tl, g,
                          a.targets, a.c, a.beta, a.lp, a.ent, sws);
       break;
-    }
-    case 4: {
-      const dim3 grid((unsigned)((a.T + 127) / 128), 4);
-      hipLaunchKernelGGL((tile_tree_kernel<2>), grid, dim3(256), 0, stream, tiles, tl, g,
+    case 4:
+      hipLaunchKernelGGL((tile_tree_kernel<2>), tgrid, dim3(128), 0, stream, tiles, tl, g,
                          a.targets, a.c, a.beta, a.lp, a.ent, sws);
       break;
-    }
-    case 8: {
-      const dim3 grid((unsigned)((a.T + 255) / 256), 8);
-      hipLaunchKernelGGL((tile_tree_kernel<1>), grid, dim3(256), 0, stream, tiles, tl, g,
+    case 8:
+      hipLaunchKernelGGL((tile_tree_kernel<1>), tgrid, dim3(64), 0, stream, tiles, tl, g,
                          a.targets, a.c, a.beta, a.lp, a.ent, sws);
       break;
-    }
     default:
       return hipErrorInvalidValue;
   }
