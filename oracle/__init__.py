@@ -1,5 +1,6 @@
-"""CPU float64 oracle (test infrastructure only; see oracle/logprob.py)."""
+"""CPU float64 oracle (test infrastructure only; see oracle/logprob.py, oracle/compare.py)."""
 from .logprob import (  # noqa: F401
     entropy, linear_logits, linear_logprob_entropy, logprob_entropy, sample_targets,
     tempered_logits,
 )
+from .compare import METRIC_NAMES, logprob_compare  # noqa: F401
