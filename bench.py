@@ -14,9 +14,11 @@ Also reported on the same JSON line:
   fused         the fused linear-logp path on the Qwen3-8B shape (T = 2048, d = 4096,
                 V = 151936 bf16) as tokens/s and fraction of the 2.5 PFLOP/s bf16
                 MFMA peak (2 T V d flops per call);
-  splits        ms per call of the logits path at vocab splits 2, 4, 8.
+  splits        ms per call of the logits path at vocab splits 2, 4, 8;
+  bf16_logits   the same rows rounded to bf16 through rlk_logprob_from_logits_bf16
+                (1024 x 303888 B per call) as GB/s against 8 TB/s.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-fused]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--no-fused]
 """
 from __future__ import annotations
 
@@ -34,7 +36,9 @@ METRIC = "tokens/s selected-logprob+entropy at V=151936; % HBM BW / % MFMA peak"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 BYTES_PER_TOKEN_LOGITS = 151936 * 4 + 8 + 8
+BYTES_PER_TOKEN_BF16 = 151936 * 2 + 8 + 8
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_reduce_T1024_V151936_traffic.json")
+TRAFFIC_FILE_BF16 = os.path.join(ROOT, "profiles", "row_reduce_bf16_T1024_V151936_traffic.json")
 TRAFFIC_SOURCES = ["entropy_rlk_logprob_amd/csrc/rlk_logits.hip",
                    "entropy_rlk_logprob_amd/csrc/rlk_state.hpp"]
 
@@ -51,12 +55,12 @@ def sources_hash(paths) -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(path: str = TRAFFIC_FILE):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None when
     there is none or the kernel source changed since the counters were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         t = json.load(f)
     if t.get("source_sha256") != sources_hash(TRAFFIC_SOURCES):
         return None
@@ -64,23 +68,23 @@ def measured_traffic():
 
 
 def time_calls(fn, steps: int, warmup: int):
-    """Mean ms per call over `steps` calls, each bracketed by HIP events recorded on the
-    current stream (the stream the library launches on); also the total wall ms."""
+    """Mean ms per call over `steps` back-to-back calls, from one pair of HIP events
+    recorded on the current stream (the stream the library launches on) around all of them;
+    also the wall-clock ms per call over the same region (host launch cost included)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record()
+    start.record()
+    for _ in range(steps):
         fn()
-        ends[i].record()
+    end.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
-    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return sum(per) / len(per), wall_ms / steps, per
+    return start.elapsed_time(end) / steps, wall_ms / steps
 
 
 def cpu_baseline(case):
@@ -97,8 +101,8 @@ def cpu_baseline(case):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -131,14 +135,14 @@ def main():
         lib.logprob_from_logits(x, t, 1.0, 1, out=(lp, ent))
 
     log(f"timing logits path: warmup {args.warmup}, steps {args.steps}")
-    k_ms, wall_ms, _ = time_calls(step, args.steps, args.warmup)
+    k_ms, wall_ms = time_calls(step, args.steps, args.warmup)
     tokens_per_s = T / (wall_ms / 1e3)
     alg_bytes = T * BYTES_PER_TOKEN_LOGITS
     achieved = alg_bytes / (k_ms / 1e3) / 1e9
     traffic = measured_traffic()
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "kernel": "row_reduce_kernel<8,true>",
+                "traffic": traffic, "kernel": "row_reduce_kernel<float,8,true>",
                 "kernel_ms": round(k_ms, 5), "algorithmic_bytes": alg_bytes}
 
     if args.copy_probe:
@@ -154,9 +158,23 @@ def main():
         ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
         fn = (lambda sp=sp, ws=ws: lib.logprob_from_logits(x, t, 1.0, sp, out=(lp, ent),
                                                            workspace=ws))
-        ms, _, _ = time_calls(fn, max(5, args.steps // 5), 2)
+        ms, _ = time_calls(fn, max(5, args.steps // 5), 10)
         splits[str(sp)] = round(ms, 5)
+
+    log("timing bf16-logits path")
+    xh = x.to(torch.bfloat16)
     del x
+    bsteps = max(5, args.steps)
+    b_ms, b_wall = time_calls(lambda: lib.logprob_from_logits(xh, t, 1.0, 1, out=(lp, ent)),
+                                 bsteps, 10)
+    b_gbs = T * BYTES_PER_TOKEN_BF16 / (b_ms / 1e3) / 1e9
+    bf16 = {"ms_per_call": round(b_ms, 5), "tokens_per_s": round(T / (b_wall / 1e3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(b_gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(b_gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(TRAFFIC_FILE_BF16),
+                         "kernel": "row_reduce_kernel<unsigned short,8,true>",
+                         "algorithmic_bytes": T * BYTES_PER_TOKEN_BF16}}
+    del xh
 
     fused = None
     if not args.no_fused:
@@ -176,7 +194,7 @@ def main():
 
         fsteps = max(5, min(args.steps, 20))
         log(f"timing fused path: steps {fsteps}")
-        f_ms, f_wall, _ = time_calls(fstep, fsteps, 2)
+        f_ms, f_wall = time_calls(fstep, fsteps, 3)
         flops = 2.0 * Tf * V * d
         tflops = flops / (f_ms / 1e3) / 1e12
         fused = {"workload": S.WORKLOADS[4].name, "n_tokens": Tf, "hidden": d, "vocab": V,
@@ -199,6 +217,7 @@ def main():
                    "parallelism": "single-gpu"},
         "backend": lib.backend_id(),
         "roofline": roofline, "cpu_baseline": cpu, "fused": fused, "splits_ms": splits,
+        "bf16_logits": bf16,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)

@@ -9,6 +9,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
+import struct
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -21,7 +22,11 @@ RLK_ERR_UNSUPPORTED_DEVICE = 2
 RLK_ERR_WORKSPACE_TOO_SMALL = 3
 RLK_ERR_HIP = 4
 
-OP_FROM_LOGITS, OP_LINEAR, OP_ENTROPY = 0, 1, 2
+OP_FROM_LOGITS, OP_LINEAR, OP_ENTROPY, OP_COMPARE = 0, 1, 2, 3
+
+# Field order of rlk_compare_result (8 x 8 bytes: four int64, then four double).
+COMPARE_FIELDS = ("active_tokens", "mismatch_count", "bitwise_mismatch_count", "reserved",
+                  "max_abs_diff", "mean_abs_diff", "mismatch_kl", "mismatch_k3_kl")
 
 
 class RlkError(RuntimeError):
@@ -39,7 +44,7 @@ def header_functions() -> list[str]:
     with open(HEADER) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z_0-9]*\s*\*?\s*(rlk_[a-z_]+)\s*\(",
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z_0-9]*\s*\*?\s*(rlk_[a-z0-9_]+)\s*\(",
                       text, flags=re.M)
 
 
@@ -72,6 +77,13 @@ class Library:
         L.rlk_entropy.restype = ctypes.c_int
         L.rlk_entropy.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, ctypes.c_float, ctypes.c_int32,
                                   _c_p, _c_p, ctypes.c_size_t, _c_p]
+        L.rlk_logprob_from_logits_bf16.restype = ctypes.c_int
+        L.rlk_logprob_from_logits_bf16.argtypes = L.rlk_logprob_from_logits.argtypes
+        L.rlk_entropy_bf16.restype = ctypes.c_int
+        L.rlk_entropy_bf16.argtypes = L.rlk_entropy.argtypes
+        L.rlk_logprob_compare.restype = ctypes.c_int
+        L.rlk_logprob_compare.argtypes = [_c_p, _c_p, _c_p, _c_i64, _c_p, _c_p,
+                                          ctypes.c_size_t, _c_p]
         L.rlk_status_string.restype = ctypes.c_char_p
         L.rlk_status_string.argtypes = [ctypes.c_int]
         L.rlk_backend_id.restype = ctypes.c_char_p
@@ -131,9 +143,11 @@ class Library:
     def logprob_from_logits(self, logits, targets, temperature: float = 1.0,
                             vocab_splits: int = 1, with_entropy: bool = True, out=None,
                             workspace=None, stream=None):
-        """logits: [T, >=V] float32 CUDA tensor (row stride = ld); targets: [T] int64."""
+        """logits: [T, >=V] float32 or bfloat16 CUDA tensor (row stride = ld);
+        targets: [T] int64."""
         import torch
-        assert logits.dtype == torch.float32 and logits.dim() == 2 and logits.stride(1) == 1
+        assert logits.dtype in (torch.float32, torch.bfloat16)
+        assert logits.dim() == 2 and logits.stride(1) == 1
         assert targets.dtype == torch.int64 and targets.is_contiguous()
         T, V = logits.shape
         dev = logits.device
@@ -142,7 +156,9 @@ class Library:
             torch.empty(T, dtype=torch.float32, device=dev) if with_entropy else None)
         ws, wsb = self._workspace(self.workspace_bytes(OP_FROM_LOGITS, T, V, 0, vocab_splits),
                                   dev, workspace)
-        st = self.lib.rlk_logprob_from_logits(
+        fn = (self.lib.rlk_logprob_from_logits if logits.dtype == torch.float32
+              else self.lib.rlk_logprob_from_logits_bf16)
+        st = fn(
             self._ptr(logits), logits.stride(0), T, V, self._ptr(targets), temperature,
             vocab_splits, self._ptr(lp), self._ptr(ent), self._ptr(ws), wsb,
             self._stream_handle(stream))
@@ -152,13 +168,15 @@ class Library:
     def entropy(self, logits, temperature: float = 1.0, vocab_splits: int = 1, out=None,
                 workspace=None, stream=None):
         import torch
-        assert logits.dtype == torch.float32 and logits.dim() == 2 and logits.stride(1) == 1
+        assert logits.dtype in (torch.float32, torch.bfloat16)
+        assert logits.dim() == 2 and logits.stride(1) == 1
         T, V = logits.shape
         ent = out if out is not None else torch.empty(T, dtype=torch.float32,
                                                       device=logits.device)
         ws, wsb = self._workspace(self.workspace_bytes(OP_ENTROPY, T, V, 0, vocab_splits),
                                   logits.device, workspace)
-        st = self.lib.rlk_entropy(self._ptr(logits), logits.stride(0), T, V, temperature,
+        fn = self.lib.rlk_entropy if logits.dtype == torch.float32 else self.lib.rlk_entropy_bf16
+        st = fn(self._ptr(logits), logits.stride(0), T, V, temperature,
                                   vocab_splits, self._ptr(ent), self._ptr(ws), wsb,
                                   self._stream_handle(stream))
         self.check(st, "rlk_entropy")
@@ -190,7 +208,42 @@ class Library:
         return lp, ent
 
 
+    def logprob_compare_async(self, train, rollout, mask=None, out=None, workspace=None,
+                              stream=None):
+        """Launch rlk_logprob_compare; returns the 64-byte device result tensor (uint8)."""
+        import torch
+        assert train.dtype == torch.float32 and rollout.dtype == torch.float32
+        assert train.dim() == 1 and train.shape == rollout.shape
+        assert train.is_contiguous() and rollout.is_contiguous()
+        if mask is not None:
+            assert mask.dtype in (torch.uint8, torch.bool) and mask.shape == train.shape
+            assert mask.is_contiguous()
+        T = train.shape[0]
+        res = out if out is not None else torch.empty(64, dtype=torch.uint8, device=train.device)
+        wsb = self.workspace_bytes(OP_COMPARE, T, 1)
+        ws, wsb = self._workspace(wsb, train.device, workspace)
+        st = self.lib.rlk_logprob_compare(self._ptr(train), self._ptr(rollout), self._ptr(mask),
+                                          T, self._ptr(res), self._ptr(ws), wsb,
+                                          self._stream_handle(stream))
+        self.check(st, "rlk_logprob_compare")
+        return res
+
+    def logprob_compare(self, train, rollout, mask=None, workspace=None, stream=None) -> dict:
+        """Comparison metrics as a dict (copies the 64-byte result to the host)."""
+        res = self.logprob_compare_async(train, rollout, mask, None, workspace, stream)
+        return unpack_compare(bytes(res.cpu().numpy().tobytes()))
+
+
 _LIB: Library | None = None
+
+
+def unpack_compare(raw: bytes) -> dict:
+    """rlk_compare_result bytes -> dict (the reserved field dropped)."""
+    ints = struct.unpack("<4q", raw[:32])
+    dbls = struct.unpack("<4d", raw[32:64])
+    out = dict(zip(COMPARE_FIELDS, ints + dbls))
+    del out["reserved"]
+    return out
 
 
 def load(path: str = LIB_PATH) -> Library:

@@ -23,6 +23,8 @@ constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxVocab = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxVocabLinear = int64_t(1) << 26;
 constexpr int64_t kMaxHidden = int64_t(1) << 20;
+// Comparison: the block count (ceil(T / 4096)) stays a valid grid size.
+constexpr int64_t kMaxCompareTokens = int64_t(1) << 40;
 // Row strides of the fused path: 256 rows x stride stays within 32-bit tile offsets.
 constexpr int64_t kMaxLdLinear = int64_t(1) << 22;
 
@@ -56,7 +58,7 @@ size_t logits_ws_bytes(int64_t T, int32_t S) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Shared validation of the logits-path calls.
-rlk_status validate_logits(const float* logits, int64_t ld, int64_t T, int64_t V,
+rlk_status validate_logits(const void* logits, int64_t ld, int64_t T, int64_t V,
                            float temperature, int32_t S, void* ws, size_t ws_bytes) {
   if (T < 0 || T > kMaxRows || V < 1 || V > kMaxVocab || ld < V) return RLK_ERR_INVALID_ARGUMENT;
   if (T > 0 && !logits) return RLK_ERR_INVALID_ARGUMENT;
@@ -70,11 +72,13 @@ rlk_status validate_logits(const float* logits, int64_t ld, int64_t T, int64_t V
   return RLK_OK;
 }
 
-rlk_status run_logits(const float* logits, int64_t ld, int64_t T, int64_t V,
-                      const int64_t* targets, float temperature, int32_t S, float* lp, float* ent,
-                      void* ws, void* stream) {
+// logits_f32 or logits_bf16 (exactly one non-null) in the same [T, ld] row-major layout.
+rlk_status run_logits(const float* logits_f32, const uint16_t* logits_bf16, int64_t ld, int64_t T,
+                      int64_t V, const int64_t* targets, float temperature, int32_t S, float* lp,
+                      float* ent, void* ws, void* stream) {
   rlk::LogitsArgs a;
-  a.X = logits;
+  a.X = logits_f32;
+  a.Xh = logits_bf16;
   a.ld = ld;
   a.T = T;
   a.V = V;
@@ -83,7 +87,8 @@ rlk_status run_logits(const float* logits, int64_t ld, int64_t T, int64_t V,
   a.beta = 1.0 / (double)temperature;
   a.c = (float)(kLog2e / (double)temperature);
   a.S = S;
-  a.vec = aligned(logits, 16) && (ld % 4 == 0);
+  a.vec = logits_f32 ? (aligned(logits_f32, 16) && ld % 4 == 0)
+                     : (aligned(logits_bf16, 8) && ld % 4 == 0);
   a.lp = lp;
   a.ent = ent;
   a.ws = static_cast<rlk::WireState*>(ws);
@@ -97,6 +102,12 @@ extern "C" {
 
 rlk_status rlk_workspace_bytes(int op, int64_t n_tokens, int64_t vocab, int64_t hidden,
                                int32_t vocab_splits, size_t* bytes_out) {
+  if (op == RLK_OP_COMPARE) {
+    if (!bytes_out || n_tokens < 0 || n_tokens > kMaxCompareTokens)
+      return RLK_ERR_INVALID_ARGUMENT;
+    *bytes_out = rlk::compare_workspace_bytes(n_tokens);
+    return RLK_OK;
+  }
   if (!bytes_out || n_tokens < 0 || n_tokens > kMaxRows || vocab < 1 ||
       !valid_splits(vocab_splits))
     return RLK_ERR_INVALID_ARGUMENT;
@@ -127,8 +138,40 @@ rlk_status rlk_logprob_from_logits(const float* logits, int64_t ld_logits, int64
   if (n_tokens == 0) return RLK_OK;
   s = check_device();
   if (s != RLK_OK) return s;
-  return run_logits(logits, ld_logits, n_tokens, vocab, target_ids, temperature, vocab_splits,
-                    logprob_out, entropy_out, workspace, stream);
+  return run_logits(logits, nullptr, ld_logits, n_tokens, vocab, target_ids, temperature,
+                    vocab_splits, logprob_out, entropy_out, workspace, stream);
+}
+
+rlk_status rlk_logprob_from_logits_bf16(const uint16_t* logits, int64_t ld_logits,
+                                        int64_t n_tokens, int64_t vocab,
+                                        const int64_t* target_ids, float temperature,
+                                        int32_t vocab_splits, float* logprob_out,
+                                        float* entropy_out, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  if (n_tokens > 0 && (!target_ids || !logprob_out)) return RLK_ERR_INVALID_ARGUMENT;
+  rlk_status s = validate_logits(logits, ld_logits, n_tokens, vocab, temperature, vocab_splits,
+                                 workspace, workspace_bytes);
+  if (s != RLK_OK) return s;
+  if (n_tokens == 0) return RLK_OK;
+  s = check_device();
+  if (s != RLK_OK) return s;
+  return run_logits(nullptr, logits, ld_logits, n_tokens, vocab, target_ids, temperature,
+                    vocab_splits, logprob_out, entropy_out, workspace, stream);
+}
+
+rlk_status rlk_entropy_bf16(const uint16_t* logits, int64_t ld_logits, int64_t n_tokens,
+                            int64_t vocab, float temperature, int32_t vocab_splits,
+                            float* entropy_out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (n_tokens > 0 && !entropy_out) return RLK_ERR_INVALID_ARGUMENT;
+  rlk_status s = validate_logits(logits, ld_logits, n_tokens, vocab, temperature, vocab_splits,
+                                 workspace, workspace_bytes);
+  if (s != RLK_OK) return s;
+  if (n_tokens == 0) return RLK_OK;
+  s = check_device();
+  if (s != RLK_OK) return s;
+  return run_logits(nullptr, logits, ld_logits, n_tokens, vocab, nullptr, temperature,
+                    vocab_splits, nullptr, entropy_out, workspace, stream);
 }
 
 rlk_status rlk_entropy(const float* logits, int64_t ld_logits, int64_t n_tokens, int64_t vocab,
@@ -141,8 +184,8 @@ rlk_status rlk_entropy(const float* logits, int64_t ld_logits, int64_t n_tokens,
   if (n_tokens == 0) return RLK_OK;
   s = check_device();
   if (s != RLK_OK) return s;
-  return run_logits(logits, ld_logits, n_tokens, vocab, nullptr, temperature, vocab_splits,
-                    nullptr, entropy_out, workspace, stream);
+  return run_logits(logits, nullptr, ld_logits, n_tokens, vocab, nullptr, temperature,
+                    vocab_splits, nullptr, entropy_out, workspace, stream);
 }
 
 rlk_status rlk_linear_logprob(const uint16_t* hidden_bf16, int64_t ld_hidden,
@@ -203,5 +246,25 @@ const char* rlk_status_string(rlk_status status) {
 }
 
 const char* rlk_backend_id(void) { return "rlk.logprob.strict.gfx950.v1"; }
+
+rlk_status rlk_logprob_compare(const float* train_logprob, const float* rollout_logprob,
+                               const uint8_t* active_mask, int64_t n_tokens,
+                               rlk_compare_result* result, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (n_tokens < 0 || n_tokens > kMaxCompareTokens || !result || !aligned(result, 8))
+    return RLK_ERR_INVALID_ARGUMENT;
+  if (n_tokens > 0 && (!train_logprob || !rollout_logprob)) return RLK_ERR_INVALID_ARGUMENT;
+  const size_t need = rlk::compare_workspace_bytes(n_tokens);
+  if (need > 0) {
+    if (!workspace) return RLK_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(workspace, 256)) return RLK_ERR_INVALID_ARGUMENT;
+  }
+  if (workspace_bytes < need) return RLK_ERR_WORKSPACE_TOO_SMALL;
+  rlk_status s = check_device();
+  if (s != RLK_OK) return s;
+  const hipError_t e = rlk::launch_compare(train_logprob, rollout_logprob, active_mask, n_tokens,
+                                           workspace, result, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RLK_OK : RLK_ERR_HIP;
+}
 
 }  // extern "C"

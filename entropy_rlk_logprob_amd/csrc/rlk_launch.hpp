@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "rlk_logprob.h"
+
 namespace rlk {
 
 struct WireState;
@@ -16,13 +18,14 @@ inline int64_t chunk_cols(int64_t V) {
 }
 
 struct LogitsArgs {
-  const float* X;
+  const float* X;          // fp32 logits, or null when Xh is given
+  const uint16_t* Xh;      // bf16 logits (bit patterns), or null
   int64_t ld, T, V, Vc;
   const int64_t* targets;  // may be null (entropy only)
   float c;                 // log2(e) / tau, rounded once to fp32
   double beta;             // 1 / tau in fp64
   int S;                   // vocab splits: 1, 2, 4, 8
-  bool vec;                // 16-byte loads legal (aligned base, ld % 4 == 0)
+  bool vec;                // quad loads legal (base aligned to a quad, ld % 4 == 0)
   float* lp;               // may be null
   float* ent;              // may be null
   WireState* ws;           // S * T wire states when S > 1
@@ -62,5 +65,12 @@ struct LinearWorkspace {
 LinearWorkspace linear_workspace_layout(int64_t T, int64_t V, int S);
 
 hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream);
+
+// Train-vs-rollout comparison (rlk_compare.hip).
+using CompareResult = rlk_compare_result;
+int64_t compare_blocks(int64_t T);
+size_t compare_workspace_bytes(int64_t T);
+hipError_t launch_compare(const float* train, const float* rollout, const uint8_t* mask,
+                          int64_t T, void* ws, CompareResult* out, hipStream_t stream);
 
 }  // namespace rlk

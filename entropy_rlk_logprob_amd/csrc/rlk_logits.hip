@@ -26,35 +26,69 @@ namespace rlk {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct Quad4 {
   float v[16];
 };
 
-template <bool VEC>
-__device__ __forceinline__ void load_quad(const float* __restrict__ p, int q, float* dst) {
-  if constexpr (VEC) {
-    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + q);
-    dst[0] = v.x;
-    dst[1] = v.y;
-    dst[2] = v.z;
-    dst[3] = v.w;
-  } else {
+// Logit element types: fp32, or bf16 given as its 16-bit pattern (widened exactly).
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// A lane's group g holds quads q = lane + 64 * (4 g + i), i = 0..3 (16 elements).  The raw
+// form keeps what one load brings in (fp32: 4 x 16 bytes; bf16: 4 x 8 bytes, still packed)
+// so that several groups can be in flight without spending 16 VGPRs on each.
+template <typename E> struct RawGroup;
+template <> struct RawGroup<float> { f32x4 q[4]; };
+template <> struct RawGroup<uint16_t> { u32x2 q[4]; };
+
+template <typename E>
+__device__ __forceinline__ void load_raw(const E* __restrict__ p, int lane, int g,
+                                         RawGroup<E>& r) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dst[j] = __builtin_nontemporal_load(p + 4 * q + j);
+  for (int i = 0; i < 4; ++i) {
+    const int q = lane + 64 * (4 * g + i);
+    if constexpr (sizeof(E) == 4)
+      r.q[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + q);
+    else
+      r.q[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p) + q);
   }
 }
 
-// Group g of a lane: quads q = lane + 64 * (4 g + i), i = 0..3, all inside the chunk.
-template <bool VEC>
-__device__ __forceinline__ void load_group_full(const float* __restrict__ p, int lane, int g,
-                                                Quad4& out) {
+template <typename E>
+__device__ __forceinline__ void widen(const RawGroup<E>& r, Quad4& out) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) load_quad<VEC>(p, lane + 64 * (4 * g + i), out.v + 4 * i);
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (sizeof(E) == 4) {
+      out.v[4 * i + 0] = r.q[i].x;
+      out.v[4 * i + 1] = r.q[i].y;
+      out.v[4 * i + 2] = r.q[i].z;
+      out.v[4 * i + 3] = r.q[i].w;
+    } else {  // little endian: the lower half of each dword is the earlier element
+      out.v[4 * i + 0] = __uint_as_float(r.q[i].x << 16);
+      out.v[4 * i + 1] = __uint_as_float(r.q[i].x & 0xffff0000u);
+      out.v[4 * i + 2] = __uint_as_float(r.q[i].y << 16);
+      out.v[4 * i + 3] = __uint_as_float(r.q[i].y & 0xffff0000u);
+    }
+  }
+}
+
+// Element loads of a full group (rows whose stride or base rule out the wide loads).
+template <typename E>
+__device__ __forceinline__ void load_group_scalar(const E* __restrict__ p, int lane, int g,
+                                                  Quad4& out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = lane + 64 * (4 * g + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out.v[4 * i + j] = to_f32(__builtin_nontemporal_load(p + 4 * q + j));
+  }
 }
 
 // Same, with columns at or beyond n replaced by -inf (the identity's contribution).
-__device__ __forceinline__ void load_group_masked(const float* __restrict__ p, int lane, int g,
+template <typename E>
+__device__ __forceinline__ void load_group_masked(const E* __restrict__ p, int lane, int g,
                                                   int n, Quad4& out) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -62,15 +96,15 @@ __device__ __forceinline__ void load_group_masked(const float* __restrict__ p, i
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int col = 4 * q + j;
-      out.v[4 * i + j] = (col < n) ? __builtin_nontemporal_load(p + col) : kNegInf;
+      out.v[4 * i + j] = (col < n) ? to_f32(__builtin_nontemporal_load(p + col)) : kNegInf;
     }
   }
 }
 
 // One workgroup = one (row, shard); WAVES = 8 / S chunks per shard, one wave per chunk.
-template <int WAVES, bool VEC>
+template <typename E, int WAVES, bool VEC>
 __global__ __launch_bounds__(64 * WAVES) void row_reduce_kernel(
-    const float* __restrict__ X, int64_t ld, int64_t T, int64_t V, int64_t Vc,
+    const E* __restrict__ X, int64_t ld, int64_t T, int64_t V, int64_t Vc,
     const int64_t* __restrict__ targets, float c, double beta, float* __restrict__ lp_out,
     float* __restrict__ ent_out, WireState* __restrict__ ws) {
   const int64_t row = blockIdx.x;
@@ -81,18 +115,31 @@ __global__ __launch_bounds__(64 * WAVES) void row_reduce_kernel(
   const int64_t lo = min(chunk * Vc, V);
   const int64_t hi = min(lo + Vc, V);
   const int n = (int)(hi - lo);
-  const float* __restrict__ p = X + row * ld + lo;
+  const E* __restrict__ p = X + row * ld + lo;
 
   State st = identity_state();
   const int n_groups = (((n + 3) >> 2) + 255) >> 8;  // ceil(ceil(n/4) / 256)
   const int n_full = (n >> 2) >> 8;                   // groups with every column inside
-  if (n_full > 0) {
-    Quad4 cur, nxt;
-    load_group_full<VEC>(p, lane, 0, cur);
+  if constexpr (VEC) {
+    // Double buffer: the loads of group g + 1 are in flight while group g is reduced.
+    // (Deeper prefetch measured no faster: at 8 waves per SIMD the bf16 kernel is bound by
+    // VALU issue, the fp32 kernel by HBM.)
+    if (n_full > 0) {
+      RawGroup<E> cur, nxt;
+      load_raw(p, lane, 0, cur);
+      for (int g = 0; g < n_full; ++g) {
+        if (g + 1 < n_full) load_raw(p, lane, g + 1, nxt);
+        Quad4 v;
+        widen(cur, v);
+        st = rlk_merge(st, leaf16(v.v, c), c);
+        cur = nxt;
+      }
+    }
+  } else {
     for (int g = 0; g < n_full; ++g) {
-      if (g + 1 < n_full) load_group_full<VEC>(p, lane, g + 1, nxt);
-      st = rlk_merge(st, leaf16(cur.v, c), c);
-      cur = nxt;
+      Quad4 v;
+      load_group_scalar(p, lane, g, v);
+      st = rlk_merge(st, leaf16(v.v, c), c);
     }
   }
   for (int g = n_full; g < n_groups; ++g) {
@@ -111,14 +158,14 @@ __global__ __launch_bounds__(64 * WAVES) void row_reduce_kernel(
   const int64_t t = targets ? targets[row] : -1;
   if constexpr (WAVES == 8) {
     const bool has = (t >= 0) && (t < V);
-    const float xt = has ? X[row * ld + t] : 0.0f;
+    const float xt = has ? to_f32(X[row * ld + t]) : 0.0f;
     rlk_finalize(r, xt, has, beta, lp_out ? lp_out + row : nullptr,
                  ent_out ? ent_out + row : nullptr);
   } else {
     const int64_t s_lo = min((int64_t)shard * WAVES * Vc, V);
     const int64_t s_hi = min(s_lo + (int64_t)WAVES * Vc, V);
     const bool mine = (t >= s_lo) && (t < s_hi);
-    const float xt = mine ? X[row * ld + t] : 0.0f;
+    const float xt = mine ? to_f32(X[row * ld + t]) : 0.0f;
     ws[(int64_t)shard * T + row] = to_wire(r, xt);
   }
 }
@@ -143,17 +190,23 @@ __global__ __launch_bounds__(256) void shard_merge_kernel(
                ent_out ? ent_out + row : nullptr);
 }
 
-template <int WAVES>
-hipError_t launch_rows(const LogitsArgs& a, hipStream_t stream) {
+template <typename E, int WAVES>
+hipError_t launch_rows_t(const E* X, const LogitsArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.T, (unsigned)(8 / WAVES));
   const dim3 block(64 * WAVES);
   if (a.vec)
-    hipLaunchKernelGGL((row_reduce_kernel<WAVES, true>), grid, block, 0, stream, a.X, a.ld, a.T,
+    hipLaunchKernelGGL((row_reduce_kernel<E, WAVES, true>), grid, block, 0, stream, X, a.ld, a.T,
                        a.V, a.Vc, a.targets, a.c, a.beta, a.lp, a.ent, a.ws);
   else
-    hipLaunchKernelGGL((row_reduce_kernel<WAVES, false>), grid, block, 0, stream, a.X, a.ld, a.T,
+    hipLaunchKernelGGL((row_reduce_kernel<E, WAVES, false>), grid, block, 0, stream, X, a.ld, a.T,
                        a.V, a.Vc, a.targets, a.c, a.beta, a.lp, a.ent, a.ws);
   return hipGetLastError();
+}
+
+template <int WAVES>
+hipError_t launch_rows(const LogitsArgs& a, hipStream_t stream) {
+  return a.Xh ? launch_rows_t<uint16_t, WAVES>(a.Xh, a, stream)
+              : launch_rows_t<float, WAVES>(a.X, a, stream);
 }
 
 }  // namespace

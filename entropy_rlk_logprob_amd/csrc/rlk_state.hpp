@@ -93,22 +93,24 @@ __device__ __forceinline__ WireState to_wire(const State& s, float xt) {
   return w;
 }
 
+// x * y with 0 * (anything) = 0 (v_mul_legacy_f32): a zero-probability term (2^a = 0 at
+// a = -inf) then adds nothing to u instead of 0 * (-inf) = NaN.  Otherwise equal to x * y.
+__device__ __attribute__((const, noconvergent)) float mul_zero_wins(float, float) __asm("llvm.amdgcn.fmul.legacy");
+
 // Leaf of 16 fp32 values v[0..15] (four quads of four): exact max m, then the fp32 terms
 // 2^a and 2^a * a with a = c (v - m) summed pairwise, within each quad and then across
 // quad pairs.  -inf entries contribute nothing; a leaf of only -inf is (-inf, 0, 0).
 __device__ __forceinline__ State leaf16(const float* v, float c) {
-  const float m0 = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-  const float m1 = fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7]));
-  const float m2 = fmaxf(fmaxf(v[8], v[9]), fmaxf(v[10], v[11]));
-  const float m3 = fmaxf(fmaxf(v[12], v[13]), fmaxf(v[14], v[15]));
-  const float mg = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+  float mg = v[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mg = fmaxf(mg, v[i]);
   const float mref = (mg == kNegInf) ? 0.0f : mg;
   float e[16], t[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const float a = (v[i] - mref) * c;
     e[i] = exp2_hw(a);
-    t[i] = e[i] * fmaxf(a, -kMaxFloat);
+    t[i] = mul_zero_wins(e[i], a);
   }
   float sq[4], uq[4];
 #pragma unroll

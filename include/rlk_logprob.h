@@ -65,10 +65,12 @@ typedef enum {
 #define RLK_OP_FROM_LOGITS 0
 #define RLK_OP_LINEAR 1
 #define RLK_OP_ENTROPY 2
+#define RLK_OP_COMPARE 3
 
 /*
  * Device workspace, in bytes, that the call `op` needs for these sizes.  Pure host
- * arithmetic (no device access).  `hidden` is ignored unless op == RLK_OP_LINEAR.
+ * arithmetic (no device access).  `hidden` is ignored unless op == RLK_OP_LINEAR;
+ * for RLK_OP_COMPARE only n_tokens is used (vocab, hidden, vocab_splits are ignored).
  * The workspace must be 256-byte aligned; its contents on entry do not matter.
  * Returns RLK_ERR_INVALID_ARGUMENT for a bad op, negative sizes or a bad split count.
  */
@@ -91,6 +93,26 @@ rlk_status rlk_logprob_from_logits(const float* logits, int64_t ld_logits, int64
                                    int64_t vocab, const int64_t* target_ids, float temperature,
                                    int32_t vocab_splits, float* logprob_out, float* entropy_out,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The same two calls on bf16 logits (16-bit patterns, [n_tokens, ld_logits] row-major):
+ * each value is widened exactly to fp32 and reduced in the canonical order of the fp32
+ * calls, so the outputs are bitwise equal to rlk_logprob_from_logits / rlk_entropy on the
+ * widened logits.  Half the HBM bytes per token.  The RL-Kernel runbook's model is BF16
+ * (issue #342, "Source and environment"), so LM-head logits can arrive in bf16.
+ * Workspace: rlk_workspace_bytes with RLK_OP_FROM_LOGITS / RLK_OP_ENTROPY (same sizes).
+ */
+rlk_status rlk_logprob_from_logits_bf16(const uint16_t* logits, int64_t ld_logits,
+                                        int64_t n_tokens, int64_t vocab,
+                                        const int64_t* target_ids, float temperature,
+                                        int32_t vocab_splits, float* logprob_out,
+                                        float* entropy_out, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+rlk_status rlk_entropy_bf16(const uint16_t* logits, int64_t ld_logits, int64_t n_tokens,
+                            int64_t vocab, float temperature, int32_t vocab_splits,
+                            float* entropy_out, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /*
  * LM-head projection fused with the selected-token logprob ("linear-logp"):
@@ -118,6 +140,47 @@ rlk_status rlk_linear_logprob(const uint16_t* hidden_bf16, int64_t ld_hidden,
 rlk_status rlk_entropy(const float* logits, int64_t ld_logits, int64_t n_tokens, int64_t vocab,
                        float temperature, int32_t vocab_splits, float* entropy_out,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Train-vs-rollout selected-logprob comparison over the active tokens: the figures the
+ * RL-Kernel h100-pcp.json evidence page reports in its train_rollout_logprob block and
+ * runtime_scalar_logprob rows, and that the RL-Kernel issue #342 runbook requires of the
+ * per-row selected-logprob comparison (section 2: mismatch count 0, max abs diff 0.0).
+ * With d = train - rollout evaluated in fp64 (exact for fp32 inputs):
+ *   active_tokens           number of tokens with active_mask != 0 (all if mask is NULL)
+ *   mismatch_count          active tokens with train != rollout as IEEE values
+ *                           (NaN on either side counts; -0 equals +0)
+ *   bitwise_mismatch_count  active tokens whose 32-bit patterns differ
+ *   max_abs_diff            max |d|  (NaN if any active d is NaN)
+ *   mean_abs_diff           sum |d| / n
+ *   mismatch_kl             sum(-d) / n                 k1 estimate of KL(rollout || train)
+ *   mismatch_k3_kl          sum(expm1(d) - d) / n       k3 estimate of KL(rollout || train)
+ * with n = active_tokens; when n = 0 every figure is 0.  The rollout engine sampled the
+ * tokens, which is why the log-ratio d estimates KL(rollout || train) this way.
+ *   train_logprob, rollout_logprob  [n_tokens] fp32 device arrays
+ *   active_mask     [n_tokens] uint8 device array or NULL
+ *   result          one rlk_compare_result in DEVICE memory (8-byte aligned), written by the
+ *                   call; unlike the other calls, n_tokens == 0 still launches one small
+ *                   kernel, to write the all-zero result
+ *   workspace       rlk_workspace_bytes(RLK_OP_COMPARE, n_tokens, ...) bytes, 256-aligned
+ * Deterministic: fixed token-to-thread mapping and a fixed combination tree, no atomics;
+ * the same inputs give the same bits on every call.
+ */
+typedef struct {
+  int64_t active_tokens;
+  int64_t mismatch_count;
+  int64_t bitwise_mismatch_count;
+  int64_t reserved;          /* written as 0 */
+  double max_abs_diff;
+  double mean_abs_diff;
+  double mismatch_kl;
+  double mismatch_k3_kl;
+} rlk_compare_result;       /* 64 bytes */
+
+rlk_status rlk_logprob_compare(const float* train_logprob, const float* rollout_logprob,
+                               const uint8_t* active_mask, int64_t n_tokens,
+                               rlk_compare_result* result, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* rlk_status_string(rlk_status status);

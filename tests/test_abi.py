@@ -11,6 +11,8 @@ from __future__ import annotations
 import ctypes
 import math
 
+import struct
+
 import pytest
 
 from entropy_rlk_logprob_amd import binding as B
@@ -31,7 +33,9 @@ def no_gpu_visible() -> bool:
 def test_exports_every_header_symbol(L):
     names = B.header_functions()
     assert set(names) == {"rlk_workspace_bytes", "rlk_logprob_from_logits", "rlk_linear_logprob",
-                          "rlk_entropy", "rlk_status_string", "rlk_backend_id"}
+                          "rlk_entropy", "rlk_status_string", "rlk_backend_id",
+                          "rlk_logprob_from_logits_bf16", "rlk_entropy_bf16",
+                          "rlk_logprob_compare"}
     for n in names:
         assert hasattr(L.lib, n), n
         assert ctypes.cast(getattr(L.lib, n), ctypes.c_void_p).value
@@ -90,12 +94,64 @@ def test_logits_validation(L, kw, code):
     assert call_logits(L, **kw) == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=None), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(ld=1000), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(tau=0.0), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(S=5), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(S=2), B.RLK_ERR_WORKSPACE_TOO_SMALL),
+    (dict(T=0, logits=None, targets=None, lp=None), B.RLK_OK),
+])
+def test_bf16_logits_validation(L, kw, code):
+    a = dict(logits=FAKE, ld=1024, T=4, V=1024, targets=FAKE, tau=1.0, S=1, lp=FAKE, ent=FAKE,
+             ws=None, wsb=0)
+    a.update(kw)
+    assert L.lib.rlk_logprob_from_logits_bf16(a["logits"], a["ld"], a["T"], a["V"], a["targets"],
+                                              a["tau"], a["S"], a["lp"], a["ent"], a["ws"],
+                                              a["wsb"], None) == code
+    if kw.get("T") != 0 and "targets" not in kw:
+        assert L.lib.rlk_entropy_bf16(a["logits"], a["ld"], a["T"], a["V"], a["tau"], a["S"],
+                                      a["ent"], a["ws"], a["wsb"], None) == code
+
+
 def test_entropy_validation(L):
     e = L.entropy_raw
     assert e(FAKE, 1024, 4, 1024, 1.0, 1, None, None, 0, None) == B.RLK_ERR_INVALID_ARGUMENT
     assert e(FAKE, 1024, 4, 1024, 1.0, 5, FAKE, None, 0, None) == B.RLK_ERR_INVALID_ARGUMENT
     assert e(FAKE, 1024, 4, 1024, 1.0, 2, FAKE, None, 0, None) == B.RLK_ERR_WORKSPACE_TOO_SMALL
     assert e(None, 1024, 0, 1024, 1.0, 1, None, None, 0, None) == B.RLK_OK
+
+
+def test_compare_workspace_and_result_layout(L):
+    assert L.workspace_bytes(B.OP_COMPARE, 0, 1) == 0
+    assert L.workspace_bytes(B.OP_COMPARE, 1, 1) == 64
+    assert L.workspace_bytes(B.OP_COMPARE, 4096, 1) == 64
+    assert L.workspace_bytes(B.OP_COMPARE, 4097, 1) == 128
+    assert L.workspace_bytes(B.OP_COMPARE, 16384, 0, 0, 3) == 4 * 64   # vocab/splits ignored
+    raw = struct.pack("<4q4d", 7, 2, 3, 0, 0.5, 0.25, -0.125, 0.0625)
+    assert B.unpack_compare(raw) == dict(active_tokens=7, mismatch_count=2,
+                                         bitwise_mismatch_count=3, max_abs_diff=0.5,
+                                         mean_abs_diff=0.25, mismatch_kl=-0.125,
+                                         mismatch_k3_kl=0.0625)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(train=None), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(rollout=None), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(res=None), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(res=FAKE + 4), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(T=-1), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(ws=None), B.RLK_ERR_WORKSPACE_TOO_SMALL),
+    (dict(wsb=127), B.RLK_ERR_WORKSPACE_TOO_SMALL),
+    (dict(ws=FAKE + 64), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(), B.RLK_ERR_UNSUPPORTED_DEVICE),                 # valid: reaches the device check
+    (dict(T=0, train=None, rollout=None, ws=None, wsb=0), B.RLK_ERR_UNSUPPORTED_DEVICE),
+])
+def test_compare_validation(L, kw, code):
+    a = dict(train=FAKE, rollout=FAKE, mask=None, T=5000, res=FAKE, ws=FAKE, wsb=128)
+    a.update(kw)
+    assert L.lib.rlk_logprob_compare(a["train"], a["rollout"], a["mask"], a["T"], a["res"],
+                                     a["ws"], a["wsb"], None) == code
 
 
 def call_linear(L, h=FAKE, ldh=2048, w=FAKE, ldw=2048, T=4, d=2048, V=1000, tg=FAKE, tau=1.0,
@@ -132,3 +188,5 @@ def test_valid_call_without_gfx950_is_unsupported_device(L):
     assert call_linear(L) == B.RLK_ERR_UNSUPPORTED_DEVICE
     assert L.entropy_raw(FAKE, 1024, 4, 1024, 1.0, 1, FAKE, None, 0, None) == \
         B.RLK_ERR_UNSUPPORTED_DEVICE
+    assert L.lib.rlk_logprob_from_logits_bf16(FAKE, 1024, 4, 1024, FAKE, 1.0, 1, FAKE, None, None,
+                                              0, None) == B.RLK_ERR_UNSUPPORTED_DEVICE
