@@ -46,6 +46,13 @@ struct alignas(16) U4 {
 };
 
 // All LDS-DMA loads of this wave have landed.
+// Scheduling groups (llvm.amdgcn.sched.group.barrier): the instructions of the current
+// scheduling region are placed in the order of the groups requested.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedVmemRead = 0x020;
+#define sched_group(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Workgroup barrier ordering LDS reads (this wave's ds_reads done, then s_barrier).  The
@@ -159,7 +166,6 @@ __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
     // whose buffer the loads of stage kt + 1 now overwrite.
     wait_dma();
     lds_barrier();
-    if (kt + 1 < nk) issue_stage((int64_t)(kt + 1) * kBK, (kt + 1) & 1);
     const char* wb = smem + (kt & 1) * kStageBytes;
     const char* hb = wb + kTileV * kBK * 2;
     // Fragments of step ks + 1 are read from LDS while the MFMAs of step ks run.
@@ -176,6 +182,11 @@ __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
             bf16x8, *reinterpret_cast<const U4*>(hb + lds_offset(wt * 64 + b * 32 + frow, c16)));
     };
     read_frags(0, 0);
+    sched_group(kSchedDsRead, 6);
+    // Loads of stage kt + 1 into the other buffer.  Issued on every stage (the last one
+    // repeats stage nk - 1 into the idle buffer) so that they stay in this scheduling
+    // region and can be spread between the MFMAs of step 0 instead of stalling the wave.
+    issue_stage((int64_t)min(kt + 1, nk - 1) * kBK, (kt + 1) & 1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       if (ks + 1 < 4) read_frags(ks + 1, (ks + 1) & 1);
@@ -185,8 +196,31 @@ __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
         for (int b = 0; b < 2; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][a], bfr[ks & 1][b],
                                                               acc[a][b], 0, 0, 0);
+      // Instruction order: step 0 interleaves its eight MFMAs with the eight loads of the
+      // next stage, then reads the fragments of step 1; steps 1 and 2 interleave the six
+      // LDS reads of the following step with their first six MFMAs.  Left to itself the
+      // scheduler merges the two fragment buffers, waits on each read right away and
+      // issues all stage loads in one burst ahead of the MFMAs.
+      if (ks == 0) {
+#pragma unroll
+        for (int q = 0; q < kBlocksPerWave; ++q) {
+          sched_group(kSchedMfma, 1);
+          sched_group(kSchedVmemRead, 1);
+        }
+        sched_group(kSchedDsRead, 6);
+      } else if (ks + 1 < 4) {
+#pragma unroll
+        for (int q = 0; q < 6; ++q) {
+          sched_group(kSchedMfma, 1);
+          sched_group(kSchedDsRead, 1);
+        }
+        sched_group(kSchedMfma, 2);
+      } else {
+        sched_group(kSchedMfma, 8);
+      }
     }
   }
+  wait_dma();  // the repeated last-stage loads land before the epilogue reuses the LDS
   __syncthreads();
 
   // ---------------------------------------------------------------- epilogue
