@@ -25,6 +25,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "rlk_launch.hpp"
 #include "rlk_state.hpp"
 
@@ -227,40 +229,55 @@ __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
   // Each lane owns tokens wt*64 + b*32 + (lane%32), b = 0, 1, and for each of them the
   // 64 vocab rows wv*128 + a*32 + 8*(i/4) + 4*(lane/32) + (i%4).
   State half_state[2];
+  // Two instantiations: only the last tile of a chunk has rows at or beyond n_valid to mask,
+  // and keeping that test out of the common one keeps its selects and copies out too.
+  auto token_epilogue = [&](auto masked) {
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int tok_in_tile = wt * 64 + b * 32 + frow;
-    const int64_t tok = t_lo + tok_in_tile;
-    const int64_t tgt = (tok < g.T && targets) ? targets[tok] : -1;
-    // Target row relative to this tile, or -1 when the target is not in the tile.
-    const int tloc = (tgt >= v_lo && tgt < v_hi) ? (int)(tgt - v_lo) : -1;
-    State leaf[4];
-    float xt = 0.0f;
+    for (int b = 0; b < 2; ++b) {
+      const int tok_in_tile = wt * 64 + b * 32 + frow;
+      const int64_t tok = t_lo + tok_in_tile;
+      const int64_t tgt = (tok < g.T && targets) ? targets[tok] : -1;
+      // Target row relative to this tile (-1 when the target is not in the tile), and
+      // relative to this wave's vocab half.  Row r of the half is held by the lanes with
+      // fhalf = (r / 4) % 2, in register i = 4 ((r / 8) % 4) + r % 4 of block a = r / 32.
+      const int tloc = (tgt >= v_lo && tgt < v_hi) ? (int)(tgt - v_lo) : -1;
+      const int r = tloc - wv * 128;
+      const bool mine = tloc >= 0 && (unsigned)r < 128u && ((r >> 2) & 1) == fhalf;
+      // Only about one token in twenty per wave has its target in this wave's rows, so
+      // the capture sits behind a branch that whole waves skip.
+      if (mine) {
+        const int idx = ((r >> 5) << 4) | (((r >> 3) & 3) << 2) | (r & 3);  // 16 a + i
+        float xt = 0.0f;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      float v[16];
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int vr = wv * 128 + a * 32 + 8 * (i >> 2) + 4 * fhalf + (i & 3);
-        v[i] = acc[a][b][i];
-        xt = (vr == tloc) ? v[i] : xt;
+          for (int i = 0; i < 16; ++i) xt = (idx == 16 * a + i) ? acc[a][b][i] : xt;
+        target_logit[tok] = xt;
       }
-      if (n_valid < kTileV) {  // workgroup-uniform: only the last tile of a chunk is short
+
+      State leaf[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        float v[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int vr = wv * 128 + a * 32 + 8 * (i >> 2) + 4 * fhalf + (i & 3);
-          v[i] = (vr < n_valid) ? v[i] : kNegInf;
+          v[i] = acc[a][b][i];
+          if constexpr (decltype(masked)::value) {
+            const int vr = wv * 128 + a * 32 + 8 * (i >> 2) + 4 * fhalf + (i & 3);
+            v[i] = (vr < n_valid) ? v[i] : kNegInf;
+          }
         }
+        leaf[a] = leaf16(v, c);
       }
-      leaf[a] = leaf16(v, c);
+      State st = rlk_merge(rlk_merge(leaf[0], leaf[1], c), rlk_merge(leaf[2], leaf[3], c), c);
+      const State o = shfl_xor_state(st, 32);
+      half_state[b] = fhalf ? rlk_merge(o, st, c) : rlk_merge(st, o, c);
     }
-    // The one lane holding the target row of this token (if it lies in this tile) stores it.
-    if (tloc >= wv * 128 && tloc < wv * 128 + 128 && ((tloc >> 2) & 1) == fhalf)
-      target_logit[tok] = xt;
-    State st = rlk_merge(rlk_merge(leaf[0], leaf[1], c), rlk_merge(leaf[2], leaf[3], c), c);
-    const State o = shfl_xor_state(st, 32);
-    half_state[b] = fhalf ? rlk_merge(o, st, c) : rlk_merge(st, o, c);
-  }
+  };
+  if (n_valid < kTileV)
+    token_epilogue(std::true_type{});
+  else
+    token_epilogue(std::false_type{});
 
   // Cross-half merge through LDS: the upper vocab half (wv = 1) publishes its states,
   // the lower half merges (lower range first) and stores the tile state.
