@@ -70,11 +70,15 @@ __device__ __forceinline__ int lds_offset(int row, int c16) {
   return row * 128 + ((c16 ^ ((row >> 1) & 7)) << 4);
 }
 
+// Binary-counter stack of the tile tree: at most floor(log2(tiles per chunk)) + 1 entries.
+// The vocabulary limit of the fused path (2^26) bounds tiles per chunk by 2^15.
+constexpr int kMaxTreeDepth = 17;
+
 struct TileGeom {
   int64_t n_vt;       // vocabulary tiles (8 * tiles_per_chunk)
   int64_t n_tt;       // token tiles
   int64_t tpc;        // tiles per chunk
-  int64_t lane_tiles; // tiles per lane in the tile tree: max(1, next_pow2(tpc) / 64)
+  int64_t block_tiles;  // tiles per block of the tile tree: max(1, P / 8), P = next_pow2(tpc)
   int64_t Vc, V, T;
 };
 
@@ -303,33 +307,35 @@ __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
 // Tiles of each chunk -> chunk state, chunks of a shard -> shard state (tree8), then
 // either the fp64 finalize (S = 1) or the shard's wire state for the cross-shard merge.
 //
-// The tile tree is the perfect binary tree over tile index, padded with identity states
-// up to P = max(64, next power of two >= tiles per chunk) leaves (merging a state with the
-// identity on its right returns it unchanged, up to the sign of a zero u).  One wave per
-// (token, chunk): lane l first folds the aligned block of P / 64 tiles it owns (binary-
-// counter stack, identities elided), then an xor-butterfly over strides 1, 2, ..., 32
-// merges neighbouring blocks, lower lane first -- the upper levels of the same tree.
-// Block: CPS waves (the shard's chunks) for one token; grid (T, S).
+// The tile tree is the perfect binary tree over tile index, padded with identity states up
+// to P = max(8, next power of two >= tiles per chunk) leaves (merging a state with the
+// identity on its right returns it unchanged, up to the sign of a zero u).  A wave serves
+// 8 consecutive tokens x 8 aligned blocks of P / 8 tiles: lane = 8 blk + token, so each
+// load instruction reads 8 runs of 8 consecutive tokens' states (192 bytes each).  A lane
+// folds its block with a binary-counter stack (identities elided) -- the subtree of that
+// block -- and an xor-butterfly over the block bits (strides 8, 16, 32; lower block first)
+// applies the top three levels.  Block: CPS waves (the shard's chunks); grid
+// (ceil(T / 8), S).
 template <int CPS>
 __global__ __launch_bounds__(64 * CPS) void tile_tree_kernel(
     const WireState* __restrict__ tile_states, const float* __restrict__ target_logit,
     TileGeom g, const int64_t* __restrict__ targets, float c, double beta,
     float* __restrict__ lp_out, float* __restrict__ ent_out, WireState* __restrict__ shard_ws) {
-  const int64_t tok = blockIdx.x;
-  const int shard = blockIdx.y;
-  const int ci = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
+  const int ci = threadIdx.x >> 6;
+  const int tl8 = lane & 7;
+  const int blk = lane >> 3;
+  const int64_t tok = (int64_t)blockIdx.x * 8 + tl8;
+  const int shard = blockIdx.y;
   const int64_t chunk = (int64_t)shard * CPS + ci;
-  __shared__ State cs[CPS];
+  __shared__ State cs[CPS][8];
 
-  const WireState* __restrict__ base = tile_states + chunk * g.tpc * g.T + tok;
-  const int64_t k0 = (int64_t)lane * g.lane_tiles;
-  const int64_t k1 = min(k0 + g.lane_tiles, g.tpc);
+  const int64_t k0 = (int64_t)blk * g.block_tiles;
+  const int64_t k1 = min(k0 + g.block_tiles, g.tpc);
   State r = identity_state();
-  if (g.lane_tiles == 1) {
-    if (k0 < k1) r = from_wire(base[k0 * g.T]);
-  } else if (k0 < k1) {
-    State stk[16];
+  if (tok < g.T && k0 < k1) {
+    const WireState* __restrict__ base = tile_states + chunk * g.tpc * g.T + tok;
+    State stk[kMaxTreeDepth];
     int top = 0;
     for (int64_t k = k0; k < k1; ++k) {
       State cur = from_wire(base[k * g.T]);
@@ -340,14 +346,17 @@ __global__ __launch_bounds__(64 * CPS) void tile_tree_kernel(
     while (top > 0) r = rlk_merge(stk[--top], r, c);
   }
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
+  for (int off = 8; off < 64; off <<= 1) {
     const State o = shfl_xor_state(r, off);
     r = (lane & off) ? rlk_merge(o, r, c) : rlk_merge(r, o, c);
   }
-  if (lane == 0) cs[ci] = r;
+  if (blk == 0) cs[ci][tl8] = r;
   __syncthreads();
-  if (threadIdx.x != 0) return;
-  const State root = tree8(cs, CPS, c);
+  if (ci != 0 || blk != 0 || tok >= g.T) return;
+  State chunks[CPS];
+#pragma unroll
+  for (int j = 0; j < CPS; ++j) chunks[j] = cs[j][tl8];
+  const State root = tree8(chunks, CPS, c);
   const int64_t t = targets ? targets[tok] : -1;
   if constexpr (CPS == 8) {
     const bool has = (t >= 0) && (t < g.V);
@@ -386,9 +395,10 @@ hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream) {
   const LinearWorkspace L = linear_workspace_layout(a.T, a.V, a.S);
   TileGeom g;
   g.tpc = L.tiles_per_chunk;
+  if (g.tpc > (int64_t(1) << (kMaxTreeDepth - 1))) return hipErrorInvalidValue;
   int64_t pow2 = 1;
   while (pow2 < g.tpc) pow2 <<= 1;
-  g.lane_tiles = pow2 > 64 ? pow2 / 64 : 1;
+  g.block_tiles = pow2 > 8 ? pow2 / 8 : 1;
   g.n_vt = L.n_tiles;
   g.n_tt = (a.T + kTileT - 1) / kTileT;
   g.Vc = a.Vc;
@@ -407,7 +417,7 @@ hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream) {
   const WireState* tiles = reinterpret_cast<const WireState*>(base + L.tile_states);
   const float* tl = reinterpret_cast<const float*>(base + L.target_logit);
   WireState* sws = reinterpret_cast<WireState*>(base + L.shard_states);
-  const dim3 tgrid((unsigned)a.T, (unsigned)a.S);
+  const dim3 tgrid((unsigned)((a.T + 7) / 8), (unsigned)a.S);
   switch (a.S) {
     case 1:
       hipLaunchKernelGGL((tile_tree_kernel<8>), tgrid, dim3(512), 0, stream, tiles, tl, g,
