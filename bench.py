@@ -16,7 +16,10 @@ Also reported on the same JSON line:
                 MFMA peak (2 T V d flops per call);
   splits        ms per call of the logits path at vocab splits 2, 4, 8;
   bf16_logits   the same rows rounded to bf16 through rlk_logprob_from_logits_bf16
-                (1024 x 303888 B per call) as GB/s against 8 TB/s.
+                (1024 x 303888 B per call) as GB/s against 8 TB/s;
+  backward      rlk_logprob_backward_from_logits on the same rows (gradient of
+                g_lp * logprob + g_ent * entropy): ms per call and GB/s over its
+                algorithmic bytes (one read of the logits, one write of the gradient).
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--no-fused]
 """
@@ -37,6 +40,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 BYTES_PER_TOKEN_LOGITS = 151936 * 4 + 8 + 8
 BYTES_PER_TOKEN_BF16 = 151936 * 2 + 8 + 8
+BYTES_PER_TOKEN_BACKWARD = 151936 * 4 * 2 + 8 + 4 + 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_reduce_T1024_V151936_traffic.json")
 TRAFFIC_FILE_BF16 = os.path.join(ROOT, "profiles", "row_reduce_bf16_T1024_V151936_traffic.json")
 TRAFFIC_SOURCES = ["entropy_rlk_logprob_amd/csrc/rlk_logits.hip",
@@ -161,6 +165,22 @@ def main():
         ms, _ = time_calls(fn, max(5, args.steps // 5), 10)
         splits[str(sp)] = round(ms, 5)
 
+    log("timing backward of the logits path")
+    gl = torch.randn(T, generator=torch.Generator().manual_seed(7)).cuda()
+    ge = torch.randn(T, generator=torch.Generator().manual_seed(8)).cuda()
+    gout = torch.empty_like(x)
+    bw_ws = torch.empty(max(1, lib.workspace_bytes(binding.OP_BACKWARD_FROM_LOGITS, T, V, 0, 1)),
+                        dtype=torch.uint8, device="cuda")
+    g_ms, g_wall = time_calls(lambda: lib.logprob_backward_from_logits(
+        x, t, 1.0, 1, gl, ge, out=gout, workspace=bw_ws), max(5, args.steps // 2), 5)
+    g_gbs = T * BYTES_PER_TOKEN_BACKWARD / (g_ms / 1e3) / 1e9
+    backward = {"ms_per_call": round(g_ms, 5), "tokens_per_s": round(T / (g_wall / 1e3), 1),
+                "kernels": "row_reduce_kernel (row states) + logits_grad_kernel",
+                "roofline": {"bound": "hbm", "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(g_gbs / HBM_PEAK_GBS, 4),
+                             "algorithmic_bytes": T * BYTES_PER_TOKEN_BACKWARD}}
+    del gout, bw_ws
+
     log("timing bf16-logits path")
     xh = x.to(torch.bfloat16)
     del x
@@ -217,7 +237,7 @@ def main():
                    "parallelism": "single-gpu"},
         "backend": lib.backend_id(),
         "roofline": roofline, "cpu_baseline": cpu, "fused": fused, "splits_ms": splits,
-        "bf16_logits": bf16,
+        "bf16_logits": bf16, "backward": backward,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)

@@ -22,7 +22,7 @@ RLK_ERR_UNSUPPORTED_DEVICE = 2
 RLK_ERR_WORKSPACE_TOO_SMALL = 3
 RLK_ERR_HIP = 4
 
-OP_FROM_LOGITS, OP_LINEAR, OP_ENTROPY, OP_COMPARE = 0, 1, 2, 3
+OP_FROM_LOGITS, OP_LINEAR, OP_ENTROPY, OP_COMPARE, OP_BACKWARD_FROM_LOGITS = 0, 1, 2, 3, 4
 
 # Field order of rlk_compare_result (8 x 8 bytes: four int64, then four double).
 COMPARE_FIELDS = ("active_tokens", "mismatch_count", "bitwise_mismatch_count", "reserved",
@@ -84,6 +84,10 @@ class Library:
         L.rlk_logprob_compare.restype = ctypes.c_int
         L.rlk_logprob_compare.argtypes = [_c_p, _c_p, _c_p, _c_i64, _c_p, _c_p,
                                           ctypes.c_size_t, _c_p]
+        L.rlk_logprob_backward_from_logits.restype = ctypes.c_int
+        L.rlk_logprob_backward_from_logits.argtypes = [
+            _c_p, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_float, ctypes.c_int32, _c_p, _c_p, _c_p,
+            _c_i64, _c_p, ctypes.c_size_t, _c_p]
         L.rlk_status_string.restype = ctypes.c_char_p
         L.rlk_status_string.argtypes = [ctypes.c_int]
         L.rlk_backend_id.restype = ctypes.c_char_p
@@ -207,6 +211,31 @@ class Library:
         self.check(st, "rlk_linear_logprob")
         return lp, ent
 
+
+    def logprob_backward_from_logits(self, logits, targets, temperature: float = 1.0,
+                                     vocab_splits: int = 1, grad_logprob=None, grad_entropy=None,
+                                     out=None, workspace=None, stream=None):
+        """Gradient of sum g_lp * logprob + g_ent * entropy w.r.t. fp32 logits [T, >=V];
+        returns `out` (new [T, V] fp32 tensor if None; may be `logits` itself)."""
+        import torch
+        assert logits.dtype == torch.float32 and logits.dim() == 2 and logits.stride(1) == 1
+        T, V = logits.shape
+        for g in (grad_logprob, grad_entropy):
+            assert g is None or (g.dtype == torch.float32 and g.shape == (T,) and
+                                 g.is_contiguous())
+        if targets is not None:
+            assert targets.dtype == torch.int64 and targets.is_contiguous()
+        grad = out if out is not None else torch.empty((T, V), dtype=torch.float32,
+                                                       device=logits.device)
+        assert grad.dtype == torch.float32 and grad.stride(1) == 1 and grad.shape == (T, V)
+        ws, wsb = self._workspace(self.workspace_bytes(OP_BACKWARD_FROM_LOGITS, T, V, 0,
+                                                       vocab_splits), logits.device, workspace)
+        st = self.lib.rlk_logprob_backward_from_logits(
+            self._ptr(logits), logits.stride(0), T, V, self._ptr(targets), temperature,
+            vocab_splits, self._ptr(grad_logprob), self._ptr(grad_entropy), self._ptr(grad),
+            grad.stride(0), self._ptr(ws), wsb, self._stream_handle(stream))
+        self.check(st, "rlk_logprob_backward_from_logits")
+        return grad
 
     def logprob_compare_async(self, train, rollout, mask=None, out=None, workspace=None,
                               stream=None):

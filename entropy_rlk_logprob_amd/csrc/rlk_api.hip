@@ -55,6 +55,13 @@ size_t logits_ws_bytes(int64_t T, int32_t S) {
   return S > 1 ? (size_t)S * (size_t)T * sizeof(rlk::WireState) : 0;
 }
 
+// Backward workspace: the forward's shard states, then one root state per row.
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t backward_root_offset(int64_t T, int32_t S) { return align256(logits_ws_bytes(T, S)); }
+size_t backward_ws_bytes(int64_t T, int32_t S) {
+  return T == 0 ? 0 : backward_root_offset(T, S) + (size_t)T * sizeof(rlk::WireState);
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Shared validation of the logits-path calls.
@@ -92,6 +99,7 @@ rlk_status run_logits(const float* logits_f32, const uint16_t* logits_bf16, int6
   a.lp = lp;
   a.ent = ent;
   a.ws = static_cast<rlk::WireState*>(ws);
+  a.root = nullptr;
   const hipError_t e = rlk::launch_logits_path(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RLK_OK : RLK_ERR_HIP;
 }
@@ -116,6 +124,10 @@ rlk_status rlk_workspace_bytes(int op, int64_t n_tokens, int64_t vocab, int64_t 
     case RLK_OP_ENTROPY:
       if (vocab > kMaxVocab) return RLK_ERR_INVALID_ARGUMENT;
       *bytes_out = logits_ws_bytes(n_tokens, vocab_splits);
+      return RLK_OK;
+    case RLK_OP_BACKWARD_FROM_LOGITS:
+      if (vocab > kMaxVocab) return RLK_ERR_INVALID_ARGUMENT;
+      *bytes_out = backward_ws_bytes(n_tokens, vocab_splits);
       return RLK_OK;
     case RLK_OP_LINEAR:
       if (vocab > kMaxVocabLinear || hidden < 0) return RLK_ERR_INVALID_ARGUMENT;
@@ -264,6 +276,53 @@ rlk_status rlk_logprob_compare(const float* train_logprob, const float* rollout_
   if (s != RLK_OK) return s;
   const hipError_t e = rlk::launch_compare(train_logprob, rollout_logprob, active_mask, n_tokens,
                                            workspace, result, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RLK_OK : RLK_ERR_HIP;
+}
+
+rlk_status rlk_logprob_backward_from_logits(const float* logits, int64_t ld_logits,
+                                            int64_t n_tokens, int64_t vocab,
+                                            const int64_t* target_ids, float temperature,
+                                            int32_t vocab_splits, const float* grad_logprob,
+                                            const float* grad_entropy, float* grad_logits,
+                                            int64_t ld_grad, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  if (n_tokens < 0 || n_tokens > kMaxRows || vocab < 1 || vocab > kMaxVocab || ld_logits < vocab ||
+      ld_grad < vocab)
+    return RLK_ERR_INVALID_ARGUMENT;
+  if (n_tokens > 0 && (!logits || !grad_logits || (grad_logprob && !target_ids)))
+    return RLK_ERR_INVALID_ARGUMENT;
+  if (grad_logits == logits && ld_grad != ld_logits) return RLK_ERR_INVALID_ARGUMENT;
+  if (!valid_temperature(temperature) || !valid_splits(vocab_splits))
+    return RLK_ERR_INVALID_ARGUMENT;
+  const size_t need = backward_ws_bytes(n_tokens, vocab_splits);
+  if (need > 0) {
+    if (!workspace) return RLK_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(workspace, 256)) return RLK_ERR_INVALID_ARGUMENT;
+  }
+  if (workspace_bytes < need) return RLK_ERR_WORKSPACE_TOO_SMALL;
+  if (n_tokens == 0) return RLK_OK;
+  rlk_status s = check_device();
+  if (s != RLK_OK) return s;
+  rlk::LogitsArgs a;
+  a.X = logits;
+  a.Xh = nullptr;
+  a.ld = ld_logits;
+  a.T = n_tokens;
+  a.V = vocab;
+  a.Vc = rlk::chunk_cols(vocab);
+  a.targets = target_ids;
+  a.beta = 1.0 / (double)temperature;
+  a.c = (float)(kLog2e / (double)temperature);
+  a.S = vocab_splits;
+  a.vec = aligned(logits, 16) && ld_logits % 4 == 0;
+  a.lp = nullptr;
+  a.ent = nullptr;
+  char* ws = static_cast<char*>(workspace);
+  a.ws = reinterpret_cast<rlk::WireState*>(ws);
+  a.root = reinterpret_cast<rlk::WireState*>(ws + backward_root_offset(n_tokens, vocab_splits));
+  const bool vec = a.vec && aligned(grad_logits, 16) && ld_grad % 4 == 0;
+  const hipError_t e = rlk::launch_logits_backward(a, grad_logprob, grad_entropy, grad_logits,
+                                                   ld_grad, vec, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RLK_OK : RLK_ERR_HIP;
 }
 

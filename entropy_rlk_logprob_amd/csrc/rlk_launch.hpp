@@ -29,15 +29,22 @@ struct LogitsArgs {
   float* lp;               // may be null
   float* ent;              // may be null
   WireState* ws;           // S * T wire states when S > 1
+  WireState* root;         // when non-null: each row's root state instead of lp / ent
 };
 
 hipError_t launch_logits_path(const LogitsArgs& a, hipStream_t stream);
 
+// Backward of the logits path (rlk_backward.hip): the row states into a.root (which must be
+// set), then the gradient G[T, ldg]; vec: 16-byte accesses legal for both X and G.
+hipError_t launch_logits_backward(const LogitsArgs& a, const float* g_lp, const float* g_ent,
+                                  float* G, int64_t ldg, bool vec, hipStream_t stream);
+
 // Top log2(S) levels of the chunk tree over S shard states ([S][T] wire states), then
-// the fp64 finalize of every row.  Shared by both paths.
+// the fp64 finalize of every row (or, when root is non-null, each row's root state).
+// Shared by both paths.
 hipError_t launch_shard_merge(const WireState* ws, int64_t T, const int64_t* targets, int64_t V,
                               int64_t shard_cols, float c, double beta, int S, float* lp,
-                              float* ent, hipStream_t stream);
+                              float* ent, WireState* root, hipStream_t stream);
 
 struct LinearArgs {
   const uint16_t* H;

@@ -441,7 +441,7 @@ hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_shard_merge(sws, a.T, a.targets, a.V, (int64_t)(8 / a.S) * a.Vc, a.c, a.beta,
-                            a.S, a.lp, a.ent, stream);
+                            a.S, a.lp, a.ent, nullptr, stream);
 }
 
 }  // namespace rlk

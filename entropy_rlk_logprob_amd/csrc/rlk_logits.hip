@@ -106,7 +106,7 @@ template <typename E, int WAVES, bool VEC>
 __global__ __launch_bounds__(64 * WAVES) void row_reduce_kernel(
     const E* __restrict__ X, int64_t ld, int64_t T, int64_t V, int64_t Vc,
     const int64_t* __restrict__ targets, float c, double beta, float* __restrict__ lp_out,
-    float* __restrict__ ent_out, WireState* __restrict__ ws) {
+    float* __restrict__ ent_out, WireState* __restrict__ ws, WireState* __restrict__ root) {
   const int64_t row = blockIdx.x;
   const int shard = blockIdx.y;
   const int wave = threadIdx.x >> 6;
@@ -159,8 +159,11 @@ __global__ __launch_bounds__(64 * WAVES) void row_reduce_kernel(
   if constexpr (WAVES == 8) {
     const bool has = (t >= 0) && (t < V);
     const float xt = has ? to_f32(X[row * ld + t]) : 0.0f;
-    rlk_finalize(r, xt, has, beta, lp_out ? lp_out + row : nullptr,
-                 ent_out ? ent_out + row : nullptr);
+    if (root)
+      root[row] = to_wire(r, xt);
+    else
+      rlk_finalize(r, xt, has, beta, lp_out ? lp_out + row : nullptr,
+                   ent_out ? ent_out + row : nullptr);
   } else {
     const int64_t s_lo = min((int64_t)shard * WAVES * Vc, V);
     const int64_t s_hi = min(s_lo + (int64_t)WAVES * Vc, V);
@@ -170,12 +173,13 @@ __global__ __launch_bounds__(64 * WAVES) void row_reduce_kernel(
   }
 }
 
-// Top of the chunk tree across S shard states, then the fp64 finalize; one thread per row.
+// Top of the chunk tree across S shard states, then the fp64 finalize (or, when root is
+// given, the row's root state); one thread per row.
 template <int S>
 __global__ __launch_bounds__(256) void shard_merge_kernel(
     const WireState* __restrict__ ws, int64_t T, const int64_t* __restrict__ targets, int64_t V,
     int64_t shard_cols, float c, double beta, float* __restrict__ lp_out,
-    float* __restrict__ ent_out) {
+    float* __restrict__ ent_out, WireState* __restrict__ root) {
   const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (row >= T) return;
   State v[S];
@@ -186,8 +190,11 @@ __global__ __launch_bounds__(256) void shard_merge_kernel(
   const bool has = (t >= 0) && (t < V);
   const int64_t owner = has ? (t / shard_cols) : 0;
   const float xt = has ? ws[owner * T + row].xt : 0.0f;
-  rlk_finalize(r, xt, has, beta, lp_out ? lp_out + row : nullptr,
-               ent_out ? ent_out + row : nullptr);
+  if (root)
+    root[row] = to_wire(r, xt);
+  else
+    rlk_finalize(r, xt, has, beta, lp_out ? lp_out + row : nullptr,
+                 ent_out ? ent_out + row : nullptr);
 }
 
 template <typename E, int WAVES>
@@ -196,10 +203,10 @@ hipError_t launch_rows_t(const E* X, const LogitsArgs& a, hipStream_t stream) {
   const dim3 block(64 * WAVES);
   if (a.vec)
     hipLaunchKernelGGL((row_reduce_kernel<E, WAVES, true>), grid, block, 0, stream, X, a.ld, a.T,
-                       a.V, a.Vc, a.targets, a.c, a.beta, a.lp, a.ent, a.ws);
+                       a.V, a.Vc, a.targets, a.c, a.beta, a.lp, a.ent, a.ws, a.root);
   else
     hipLaunchKernelGGL((row_reduce_kernel<E, WAVES, false>), grid, block, 0, stream, X, a.ld, a.T,
-                       a.V, a.Vc, a.targets, a.c, a.beta, a.lp, a.ent, a.ws);
+                       a.V, a.Vc, a.targets, a.c, a.beta, a.lp, a.ent, a.ws, a.root);
   return hipGetLastError();
 }
 
@@ -222,25 +229,25 @@ hipError_t launch_logits_path(const LogitsArgs& a, hipStream_t stream) {
   }
   if (e != hipSuccess) return e;
   return launch_shard_merge(a.ws, a.T, a.targets, a.V, (int64_t)(8 / a.S) * a.Vc, a.c, a.beta,
-                            a.S, a.lp, a.ent, stream);
+                            a.S, a.lp, a.ent, a.root, stream);
 }
 
 hipError_t launch_shard_merge(const WireState* ws, int64_t T, const int64_t* targets, int64_t V,
                               int64_t shard_cols, float c, double beta, int S, float* lp,
-                              float* ent, hipStream_t stream) {
+                              float* ent, WireState* root, hipStream_t stream) {
   const dim3 grid((unsigned)((T + 255) / 256));
   switch (S) {
     case 2:
       hipLaunchKernelGGL((shard_merge_kernel<2>), grid, dim3(256), 0, stream, ws, T, targets, V,
-                         shard_cols, c, beta, lp, ent);
+                         shard_cols, c, beta, lp, ent, root);
       break;
     case 4:
       hipLaunchKernelGGL((shard_merge_kernel<4>), grid, dim3(256), 0, stream, ws, T, targets, V,
-                         shard_cols, c, beta, lp, ent);
+                         shard_cols, c, beta, lp, ent, root);
       break;
     case 8:
       hipLaunchKernelGGL((shard_merge_kernel<8>), grid, dim3(256), 0, stream, ws, T, targets, V,
-                         shard_cols, c, beta, lp, ent);
+                         shard_cols, c, beta, lp, ent, root);
       break;
     default:
       return hipErrorInvalidValue;

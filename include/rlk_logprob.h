@@ -66,6 +66,7 @@ typedef enum {
 #define RLK_OP_LINEAR 1
 #define RLK_OP_ENTROPY 2
 #define RLK_OP_COMPARE 3
+#define RLK_OP_BACKWARD_FROM_LOGITS 4
 
 /*
  * Device workspace, in bytes, that the call `op` needs for these sizes.  Pure host
@@ -140,6 +141,36 @@ rlk_status rlk_linear_logprob(const uint16_t* hidden_bf16, int64_t ld_hidden,
 rlk_status rlk_entropy(const float* logits, int64_t ld_logits, int64_t n_tokens, int64_t vocab,
                        float temperature, int32_t vocab_splits, float* entropy_out,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of the logits path: the gradient of  sum_r g_lp[r] logprob[r] + g_ent[r] entropy[r]
+ * with respect to the fp32 logits, for the logprob and entropy rlk_logprob_from_logits
+ * computes.  Training consumes both (the RL-Kernel h100-pcp.json evidence page's train/loss,
+ * entropy_loss and grad_norm records; its comparison block finds the trained weights and
+ * norms equal across parallel configurations, so the gradient must be deterministic):
+ *     grad[r, i] = ( g_lp[r] (delta(i, t_r) - p_i) - g_ent[r] p_i (log p_i + H_r) ) / tau
+ * with p = softmax(logits[r] / tau) and H_r the row's entropy (p log p taken as 0 at p = 0).
+ *   logits, ld_logits, n_tokens, vocab, target_ids, temperature, vocab_splits: as for
+ *                   rlk_logprob_from_logits (target_ids may be NULL if grad_logprob is NULL)
+ *   grad_logprob    [n_tokens] fp32 upstream gradient of each row's logprob, or NULL (= 0)
+ *   grad_entropy    [n_tokens] fp32 upstream gradient of each row's entropy, or NULL (= 0)
+ *   grad_logits     [n_tokens, ld_grad] fp32 output, ld_grad >= vocab; it may be the logits
+ *                   array itself (in place) when ld_grad == ld_logits, and must not
+ *                   otherwise overlap it
+ *   workspace       rlk_workspace_bytes(RLK_OP_BACKWARD_FROM_LOGITS, ...) bytes, 256-aligned
+ * Row rules: a row whose two upstream gradients are both 0 gets all zeros; otherwise a row
+ * whose forward outputs are NaN (NaN or +inf logit, all logits -inf), or whose target lies
+ * outside [0, vocab) while grad_logprob is non-zero, gets NaN.  The gradient is bitwise
+ * independent of the batch, the row order and vocab_splits: every element depends only on
+ * its own logit and the row's canonical state.
+ */
+rlk_status rlk_logprob_backward_from_logits(const float* logits, int64_t ld_logits,
+                                            int64_t n_tokens, int64_t vocab,
+                                            const int64_t* target_ids, float temperature,
+                                            int32_t vocab_splits, const float* grad_logprob,
+                                            const float* grad_entropy, float* grad_logits,
+                                            int64_t ld_grad, void* workspace,
+                                            size_t workspace_bytes, void* stream);
 
 /*
  * Train-vs-rollout selected-logprob comparison over the active tokens: the figures the

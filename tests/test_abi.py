@@ -35,7 +35,7 @@ def test_exports_every_header_symbol(L):
     assert set(names) == {"rlk_workspace_bytes", "rlk_logprob_from_logits", "rlk_linear_logprob",
                           "rlk_entropy", "rlk_status_string", "rlk_backend_id",
                           "rlk_logprob_from_logits_bf16", "rlk_entropy_bf16",
-                          "rlk_logprob_compare"}
+                          "rlk_logprob_compare", "rlk_logprob_backward_from_logits"}
     for n in names:
         assert hasattr(L.lib, n), n
         assert ctypes.cast(getattr(L.lib, n), ctypes.c_void_p).value
@@ -152,6 +152,38 @@ def test_compare_validation(L, kw, code):
     a.update(kw)
     assert L.lib.rlk_logprob_compare(a["train"], a["rollout"], a["mask"], a["T"], a["res"],
                                      a["ws"], a["wsb"], None) == code
+
+
+def test_backward_workspace(L):
+    assert L.workspace_bytes(B.OP_BACKWARD_FROM_LOGITS, 0, 100, 0, 1) == 0
+    assert L.workspace_bytes(B.OP_BACKWARD_FROM_LOGITS, 1024, 151936, 0, 1) == 1024 * 24
+    assert L.workspace_bytes(B.OP_BACKWARD_FROM_LOGITS, 1024, 151936, 0, 4) == 4 * 1024 * 24 + 1024 * 24
+    assert L.workspace_bytes(B.OP_BACKWARD_FROM_LOGITS, 10, 100, 0, 2) == 512 + 240
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=None), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(grad=None), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(ld=1000), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(ldg=1000), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(targets=None), B.RLK_ERR_INVALID_ARGUMENT),            # grad_logprob without targets
+    (dict(targets=None, glp=None), B.RLK_ERR_UNSUPPORTED_DEVICE),  # entropy-only: valid
+    (dict(grad=FAKE, ldg=1028), B.RLK_ERR_INVALID_ARGUMENT),       # in place with another ld
+    (dict(tau=-1.0), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(S=3), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(ws=None), B.RLK_ERR_WORKSPACE_TOO_SMALL),
+    (dict(wsb=4 * 24 - 1), B.RLK_ERR_WORKSPACE_TOO_SMALL),
+    (dict(ws=FAKE + 16), B.RLK_ERR_INVALID_ARGUMENT),
+    (dict(T=0, logits=None, grad=None, ws=None, wsb=0), B.RLK_OK),
+    (dict(), B.RLK_ERR_UNSUPPORTED_DEVICE),
+])
+def test_backward_validation(L, kw, code):
+    a = dict(logits=FAKE, ld=1024, T=4, V=1024, targets=FAKE, tau=1.0, S=1, glp=FAKE, gent=None,
+             grad=FAKE + 0x100000, ldg=1024, ws=FAKE, wsb=4 * 24)
+    a.update(kw)
+    assert L.lib.rlk_logprob_backward_from_logits(
+        a["logits"], a["ld"], a["T"], a["V"], a["targets"], a["tau"], a["S"], a["glp"],
+        a["gent"], a["grad"], a["ldg"], a["ws"], a["wsb"], None) == code
 
 
 def call_linear(L, h=FAKE, ldh=2048, w=FAKE, ldw=2048, T=4, d=2048, V=1000, tg=FAKE, tau=1.0,
