@@ -23,6 +23,7 @@ RLK_ERR_WORKSPACE_TOO_SMALL = 3
 RLK_ERR_HIP = 4
 
 OP_FROM_LOGITS, OP_LINEAR, OP_ENTROPY, OP_COMPARE, OP_BACKWARD_FROM_LOGITS = 0, 1, 2, 3, 4
+OP_LINEAR_BACKWARD = 5
 
 # Field order of rlk_compare_result (8 x 8 bytes: four int64, then four double).
 COMPARE_FIELDS = ("active_tokens", "mismatch_count", "bitwise_mismatch_count", "reserved",
@@ -88,6 +89,10 @@ class Library:
         L.rlk_logprob_backward_from_logits.argtypes = [
             _c_p, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_float, ctypes.c_int32, _c_p, _c_p, _c_p,
             _c_i64, _c_p, ctypes.c_size_t, _c_p]
+        L.rlk_linear_logprob_backward.restype = ctypes.c_int
+        L.rlk_linear_logprob_backward.argtypes = [
+            _c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_float,
+            ctypes.c_int32, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64, _c_p, ctypes.c_size_t, _c_p]
         L.rlk_status_string.restype = ctypes.c_char_p
         L.rlk_status_string.argtypes = [ctypes.c_int]
         L.rlk_backend_id.restype = ctypes.c_char_p
@@ -236,6 +241,39 @@ class Library:
             grad.stride(0), self._ptr(ws), wsb, self._stream_handle(stream))
         self.check(st, "rlk_logprob_backward_from_logits")
         return grad
+
+    def linear_logprob_backward(self, hidden, weight, targets, temperature: float = 1.0,
+                                vocab_splits: int = 1, grad_logprob=None, grad_entropy=None,
+                                need_hidden: bool = True, need_weight: bool = True, out=None,
+                                workspace=None, stream=None):
+        """Gradients (dH [T, d], dW [V, d], fp32; None where not requested) of
+        sum g_lp * logprob + g_ent * entropy for logits = hidden @ weight^T (bf16 bits)."""
+        import torch
+        assert hidden.dim() == 2 and weight.dim() == 2
+        assert hidden.element_size() == 2 and weight.element_size() == 2
+        assert hidden.stride(1) == 1 and weight.stride(1) == 1
+        T, d = hidden.shape
+        V, d2 = weight.shape
+        assert d == d2
+        dev = hidden.device
+        for g in (grad_logprob, grad_entropy):
+            assert g is None or (g.dtype == torch.float32 and g.shape == (T,) and
+                                 g.is_contiguous())
+        if out is not None:
+            dh, dw = out
+        else:
+            dh = torch.empty((T, d), dtype=torch.float32, device=dev) if need_hidden else None
+            dw = torch.empty((V, d), dtype=torch.float32, device=dev) if need_weight else None
+        ws, wsb = self._workspace(self.workspace_bytes(OP_LINEAR_BACKWARD, T, V, d, vocab_splits),
+                                  dev, workspace)
+        st = self.lib.rlk_linear_logprob_backward(
+            self._ptr(hidden), hidden.stride(0), self._ptr(weight), weight.stride(0), T, d, V,
+            self._ptr(targets), temperature, vocab_splits, self._ptr(grad_logprob),
+            self._ptr(grad_entropy), self._ptr(dh), dh.stride(0) if dh is not None else 0,
+            self._ptr(dw), dw.stride(0) if dw is not None else 0, self._ptr(ws), wsb,
+            self._stream_handle(stream))
+        self.check(st, "rlk_linear_logprob_backward")
+        return dh, dw
 
     def logprob_compare_async(self, train, rollout, mask=None, out=None, workspace=None,
                               stream=None):

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "librlk_logprob.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["rlk_api.hip", "rlk_logits.hip", "rlk_linear.hip", "rlk_compare.hip", "rlk_backward.hip"]
+SOURCES = ["rlk_api.hip", "rlk_logits.hip", "rlk_linear.hip", "rlk_compare.hip", "rlk_backward.hip",
+           "rlk_linear_bwd.hip"]
 ARCH = "gfx950"
 
 

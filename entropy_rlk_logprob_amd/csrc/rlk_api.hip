@@ -129,6 +129,13 @@ rlk_status rlk_workspace_bytes(int op, int64_t n_tokens, int64_t vocab, int64_t 
       if (vocab > kMaxVocab) return RLK_ERR_INVALID_ARGUMENT;
       *bytes_out = backward_ws_bytes(n_tokens, vocab_splits);
       return RLK_OK;
+    case RLK_OP_LINEAR_BACKWARD:
+      if (vocab > kMaxVocabLinear || hidden < 64 || hidden > kMaxHidden || hidden % 64 != 0)
+        return RLK_ERR_INVALID_ARGUMENT;
+      *bytes_out = n_tokens == 0
+                       ? 0
+                       : rlk::linear_backward_layout(n_tokens, vocab, hidden, vocab_splits).total;
+      return RLK_OK;
     case RLK_OP_LINEAR:
       if (vocab > kMaxVocabLinear || hidden < 0) return RLK_ERR_INVALID_ARGUMENT;
       *bytes_out = n_tokens == 0 ? 0
@@ -242,6 +249,7 @@ rlk_status rlk_linear_logprob(const uint16_t* hidden_bf16, int64_t ld_hidden,
   a.lp = logprob_out;
   a.ent = entropy_out;
   a.ws = workspace;
+  a.root = nullptr;
   const hipError_t e = rlk::launch_linear_path(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RLK_OK : RLK_ERR_HIP;
 }
@@ -323,6 +331,61 @@ rlk_status rlk_logprob_backward_from_logits(const float* logits, int64_t ld_logi
   const bool vec = a.vec && aligned(grad_logits, 16) && ld_grad % 4 == 0;
   const hipError_t e = rlk::launch_logits_backward(a, grad_logprob, grad_entropy, grad_logits,
                                                    ld_grad, vec, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RLK_OK : RLK_ERR_HIP;
+}
+
+rlk_status rlk_linear_logprob_backward(const uint16_t* hidden_bf16, int64_t ld_hidden,
+                                       const uint16_t* weight_bf16, int64_t ld_weight,
+                                       int64_t n_tokens, int64_t hidden_dim, int64_t vocab,
+                                       const int64_t* target_ids, float temperature,
+                                       int32_t vocab_splits, const float* grad_logprob,
+                                       const float* grad_entropy, float* grad_hidden,
+                                       int64_t ld_grad_hidden, float* grad_weight,
+                                       int64_t ld_grad_weight, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  if (n_tokens < 0 || n_tokens > kMaxRows || vocab < 1 || vocab > kMaxVocabLinear)
+    return RLK_ERR_INVALID_ARGUMENT;
+  if (hidden_dim < 64 || hidden_dim > kMaxHidden || hidden_dim % 64 != 0)
+    return RLK_ERR_INVALID_ARGUMENT;
+  if (ld_hidden < hidden_dim || ld_weight < hidden_dim || ld_hidden % 8 != 0 ||
+      ld_weight % 8 != 0 || ld_hidden > kMaxLdLinear || ld_weight > kMaxLdLinear)
+    return RLK_ERR_INVALID_ARGUMENT;
+  if ((grad_hidden && ld_grad_hidden < hidden_dim) || (grad_weight && ld_grad_weight < hidden_dim))
+    return RLK_ERR_INVALID_ARGUMENT;
+  if (!valid_temperature(temperature) || !valid_splits(vocab_splits))
+    return RLK_ERR_INVALID_ARGUMENT;
+  if (n_tokens > 0) {
+    if (!hidden_bf16 || !weight_bf16 || (grad_logprob && !target_ids))
+      return RLK_ERR_INVALID_ARGUMENT;
+    if (!aligned(hidden_bf16, 16) || !aligned(weight_bf16, 16)) return RLK_ERR_INVALID_ARGUMENT;
+    const size_t need =
+        rlk::linear_backward_layout(n_tokens, vocab, hidden_dim, vocab_splits).total;
+    if (workspace && !aligned(workspace, 256)) return RLK_ERR_INVALID_ARGUMENT;
+    if (!workspace || workspace_bytes < need) return RLK_ERR_WORKSPACE_TOO_SMALL;
+  }
+  if (n_tokens == 0 || (!grad_hidden && !grad_weight)) return RLK_OK;
+  rlk_status s = check_device();
+  if (s != RLK_OK) return s;
+  rlk::LinearArgs a;
+  a.H = hidden_bf16;
+  a.W = weight_bf16;
+  a.ldh = ld_hidden;
+  a.ldw = ld_weight;
+  a.T = n_tokens;
+  a.d = hidden_dim;
+  a.V = vocab;
+  a.Vc = rlk::chunk_cols(vocab);
+  a.targets = target_ids;
+  a.beta = 1.0 / (double)temperature;
+  a.c = (float)(kLog2e / (double)temperature);
+  a.S = vocab_splits;
+  a.lp = nullptr;
+  a.ent = nullptr;
+  a.ws = workspace;
+  a.root = nullptr;
+  const hipError_t e =
+      rlk::launch_linear_backward(a, grad_logprob, grad_entropy, grad_hidden, ld_grad_hidden,
+                                  grad_weight, ld_grad_weight, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RLK_OK : RLK_ERR_HIP;
 }
 

@@ -57,6 +57,7 @@ struct LinearArgs {
   float* lp;
   float* ent;
   void* ws;  // tile states, target logits, shard states
+  WireState* root;  // when non-null: each token's root state instead of lp / ent
 };
 
 // Workspace layout of the fused path (offsets in bytes from the workspace base).
@@ -72,6 +73,27 @@ struct LinearWorkspace {
 LinearWorkspace linear_workspace_layout(int64_t T, int64_t V, int S);
 
 hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream);
+
+// Fused-path backward (rlk_linear_bwd.hip).  Workspace: the forward layout, then the
+// regions below (byte offsets from the workspace base).
+struct LinearBackwardWorkspace {
+  int64_t Vp, Tp;  // V and T rounded up to multiples of 64 (K padding of the NT GEMMs)
+  size_t root;     // T root states
+  size_t rowc;     // T per-token gradient constants
+  size_t wt;       // W^T [d, Vp] bf16
+  size_t ht;       // H^T [d, Tp] bf16
+  size_t dx;       // dX [T, Vp] bf16
+  size_t dxt;      // dX^T [V, Tp] bf16
+  size_t part;     // 8 split-K partials of dH [T, d] fp32
+  size_t total;
+};
+
+LinearBackwardWorkspace linear_backward_layout(int64_t T, int64_t V, int64_t d, int S);
+
+// dH [T, ld_dh] and / or dW [V, ld_dw] (either may be null); a.ws holds the workspace.
+hipError_t launch_linear_backward(const LinearArgs& a, const float* g_lp, const float* g_ent,
+                                  float* dH, int64_t ld_dh, float* dW, int64_t ld_dw,
+                                  hipStream_t stream);
 
 // Train-vs-rollout comparison (rlk_compare.hip).
 using CompareResult = rlk_compare_result;

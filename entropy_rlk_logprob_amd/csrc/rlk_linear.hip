@@ -28,47 +28,20 @@
 #include <type_traits>
 
 #include "rlk_launch.hpp"
+#include "rlk_mma_tile.hpp"
 #include "rlk_state.hpp"
 
 namespace rlk {
 
 namespace {
 
-constexpr int kTileV = 256;   // vocab rows per tile
-constexpr int kTileT = 256;   // tokens per tile
-constexpr int kBK = 64;       // hidden elements per K step
-constexpr int kThreads = 512; // 8 waves
-constexpr int kStageBytes = (kTileV + kTileT) * kBK * 2;  // 64 KiB
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-
-struct alignas(16) U4 {
-  uint32_t x, y, z, w;
-};
-
-// All LDS-DMA loads of this wave have landed.
-// Scheduling groups (llvm.amdgcn.sched.group.barrier): the instructions of the current
-// scheduling region are placed in the order of the groups requested.
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
-constexpr int kSchedVmemRead = 0x020;
-#define sched_group(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
-
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Workgroup barrier ordering LDS reads (this wave's ds_reads done, then s_barrier).  The
-// LDS-DMA stage that the next step reads was waited for by every wave before it arrives.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// LDS slab layout: rows of kBK bf16 = 128 bytes; 16-byte column c16 of row r sits at
-// physical column c16 ^ ((r / 2) % 8).  The XOR key makes the 16 rows that one 16-lane
-// ds_read_b128 pass touches land in 16 distinct 16-byte bank groups of the 64-bank LDS.
-__device__ __forceinline__ int lds_offset(int row, int c16) {
-  return row * 128 + ((c16 ^ ((row >> 1) & 7)) << 4);
-}
+using mma::bf16x8;
+using mma::floatx16;
+using mma::kBK;
+using mma::kStageBytes;
+using mma::kThreads;
+using mma::kTileT;
+using mma::kTileV;
 
 // Binary-counter stack of the tile tree: at most floor(log2(tiles per chunk)) + 1 entries.
 // The vocabulary limit of the fused path (2^26) bounds tiles per chunk by 2^15.
@@ -120,41 +93,6 @@ __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
   const int wv = wave >> 2;  // vocab half (0, 1)
   const int wt = wave & 3;   // token quarter (0..3)
 
-  // Global -> LDS: direct 16-byte-per-lane loads into LDS (global_load_lds_dwordx4).  One
-  // wave instruction fills one 1 KiB block = 8 slab rows: lane l writes physical column
-  // l % 8 of row r = 8 b + l / 8 of block b, so it fetches logical column
-  // (l % 8) ^ ((r / 2) % 8), the layout of lds_offset().  Blocks 0..31 are the W slab,
-  // 32..63 the H slab; wave w fills blocks w, w + 8, ..., w + 56.  Offsets are
-  // tile-relative on workgroup-uniform bases; rows beyond the valid range are clamped to
-  // the last valid row (their values are masked in the epilogue or never stored).
-  constexpr int kBlocksPerWave = (kTileV + kTileT) / 8 / (kThreads / 64);  // 8
-  constexpr int kWBlocks = kTileV / 8;
-  const uint16_t* __restrict__ Wt = W + v_lo * ldw;
-  const uint16_t* __restrict__ Ht = H + t_lo * ldh;
-  const int w_last = (int)min(g.V - 1 - v_lo, (int64_t)(kTileV - 1));
-  const int h_last = (int)min(g.T - 1 - t_lo, (int64_t)(kTileT - 1));
-  int src_off[kBlocksPerWave];
-#pragma unroll
-  for (int i = 0; i < kBlocksPerWave; ++i) {
-    const int blk = i * 8 + wave;
-    const bool is_w = i < kWBlocks / 8;
-    const int bb = is_w ? blk : blk - kWBlocks;
-    const int row = bb * 8 + (lane >> 3);
-    const int col = ((lane & 7) ^ ((row >> 1) & 7)) * 8;
-    src_off[i] = is_w ? (min(row, w_last) * (int)ldw + col) : (min(row, h_last) * (int)ldh + col);
-  }
-  auto issue_stage = [&](int64_t k0, int stage) {
-#pragma unroll
-    for (int i = 0; i < kBlocksPerWave; ++i) {
-      const int blk = i * 8 + wave;
-      const bool is_w = i < kWBlocks / 8;
-      const uint16_t* src = (is_w ? Wt : Ht) + k0 + src_off[i];
-      char* dst = smem + stage * kStageBytes + blk * 1024;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-    }
-  };
-
   floatx16 acc[4][2];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -162,72 +100,13 @@ __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
-
-  const int nk = (int)(d / kBK);
+  const int w_last = (int)min(g.V - 1 - v_lo, (int64_t)(kTileV - 1));
+  const int h_last = (int)min(g.T - 1 - t_lo, (int64_t)(kTileT - 1));
+  mma::mma_tile(W + v_lo * ldw, ldw, w_last, H + t_lo * ldh, ldh, h_last, 0, (int)(d / kBK), smem,
+                acc);
+  __syncthreads();
   const int frow = lane & 31;
   const int fhalf = lane >> 5;
-  issue_stage(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    // Stage kt has landed for every wave, and every wave is done reading stage kt - 1,
-    // whose buffer the loads of stage kt + 1 now overwrite.
-    wait_dma();
-    lds_barrier();
-    const char* wb = smem + (kt & 1) * kStageBytes;
-    const char* hb = wb + kTileV * kBK * 2;
-    // Fragments of step ks + 1 are read from LDS while the MFMAs of step ks run.
-    bf16x8 af[2][4], bfr[2][2];
-    auto read_frags = [&](int ks, int buf) {
-      const int c16 = 2 * ks + fhalf;
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-        af[buf][a] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const U4*>(wb + lds_offset(wv * 128 + a * 32 + frow, c16)));
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-        bfr[buf][b] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const U4*>(hb + lds_offset(wt * 64 + b * 32 + frow, c16)));
-    };
-    read_frags(0, 0);
-    sched_group(kSchedDsRead, 6);
-    // Loads of stage kt + 1 into the other buffer.  Issued on every stage (the last one
-    // repeats stage nk - 1 into the idle buffer) so that they stay in this scheduling
-    // region and can be spread between the MFMAs of step 0 instead of stalling the wave.
-    issue_stage((int64_t)min(kt + 1, nk - 1) * kBK, (kt + 1) & 1);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks + 1 < 4) read_frags(ks + 1, (ks + 1) & 1);
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][a], bfr[ks & 1][b],
-                                                              acc[a][b], 0, 0, 0);
-      // Instruction order: step 0 interleaves its eight MFMAs with the eight loads of the
-      // next stage, then reads the fragments of step 1; steps 1 and 2 interleave the six
-      // LDS reads of the following step with their first six MFMAs.  Left to itself the
-      // scheduler merges the two fragment buffers, waits on each read right away and
-      // issues all stage loads in one burst ahead of the MFMAs.
-      if (ks == 0) {
-#pragma unroll
-        for (int q = 0; q < kBlocksPerWave; ++q) {
-          sched_group(kSchedMfma, 1);
-          sched_group(kSchedVmemRead, 1);
-        }
-        sched_group(kSchedDsRead, 6);
-      } else if (ks + 1 < 4) {
-#pragma unroll
-        for (int q = 0; q < 6; ++q) {
-          sched_group(kSchedMfma, 1);
-          sched_group(kSchedDsRead, 1);
-        }
-        sched_group(kSchedMfma, 2);
-      } else {
-        sched_group(kSchedMfma, 8);
-      }
-    }
-  }
-  wait_dma();  // the repeated last-stage loads land before the epilogue reuses the LDS
-  __syncthreads();
 
   // ---------------------------------------------------------------- epilogue
   // Each lane owns tokens wt*64 + b*32 + (lane%32), b = 0, 1, and for each of them the
@@ -320,7 +199,8 @@ template <int CPS>
 __global__ __launch_bounds__(64 * CPS) void tile_tree_kernel(
     const WireState* __restrict__ tile_states, const float* __restrict__ target_logit,
     TileGeom g, const int64_t* __restrict__ targets, float c, double beta,
-    float* __restrict__ lp_out, float* __restrict__ ent_out, WireState* __restrict__ shard_ws) {
+    float* __restrict__ lp_out, float* __restrict__ ent_out, WireState* __restrict__ shard_ws,
+    WireState* __restrict__ root) {
   const int lane = threadIdx.x & 63;
   const int ci = threadIdx.x >> 6;
   const int tl8 = lane & 7;
@@ -356,18 +236,21 @@ __global__ __launch_bounds__(64 * CPS) void tile_tree_kernel(
   State chunks[CPS];
 #pragma unroll
   for (int j = 0; j < CPS; ++j) chunks[j] = cs[j][tl8];
-  const State root = tree8(chunks, CPS, c);
+  const State top_state = tree8(chunks, CPS, c);
   const int64_t t = targets ? targets[tok] : -1;
   if constexpr (CPS == 8) {
     const bool has = (t >= 0) && (t < g.V);
     const float xt = has ? target_logit[tok] : 0.0f;
-    rlk_finalize(root, xt, has, beta, lp_out ? lp_out + tok : nullptr,
-                 ent_out ? ent_out + tok : nullptr);
+    if (root)
+      root[tok] = to_wire(top_state, xt);
+    else
+      rlk_finalize(top_state, xt, has, beta, lp_out ? lp_out + tok : nullptr,
+                   ent_out ? ent_out + tok : nullptr);
   } else {
     const int64_t s_lo = min((int64_t)shard * CPS * g.Vc, g.V);
     const int64_t s_hi = min(s_lo + (int64_t)CPS * g.Vc, g.V);
     const bool mine = (t >= s_lo) && (t < s_hi);
-    shard_ws[(int64_t)shard * g.T + tok] = to_wire(root, mine ? target_logit[tok] : 0.0f);
+    shard_ws[(int64_t)shard * g.T + tok] = to_wire(top_state, mine ? target_logit[tok] : 0.0f);
   }
 }
 
@@ -421,19 +304,19 @@ hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream) {
   switch (a.S) {
     case 1:
       hipLaunchKernelGGL((tile_tree_kernel<8>), tgrid, dim3(512), 0, stream, tiles, tl, g,
-                         a.targets, a.c, a.beta, a.lp, a.ent, sws);
+                         a.targets, a.c, a.beta, a.lp, a.ent, sws, a.root);
       return hipGetLastError();
     case 2:
       hipLaunchKernelGGL((tile_tree_kernel<4>), tgrid, dim3(256), 0, stream, tiles, tl, g,
-                         a.targets, a.c, a.beta, a.lp, a.ent, sws);
+                         a.targets, a.c, a.beta, a.lp, a.ent, sws, a.root);
       break;
     case 4:
       hipLaunchKernelGGL((tile_tree_kernel<2>), tgrid, dim3(128), 0, stream, tiles, tl, g,
-                         a.targets, a.c, a.beta, a.lp, a.ent, sws);
+                         a.targets, a.c, a.beta, a.lp, a.ent, sws, a.root);
       break;
     case 8:
       hipLaunchKernelGGL((tile_tree_kernel<1>), tgrid, dim3(64), 0, stream, tiles, tl, g,
-                         a.targets, a.c, a.beta, a.lp, a.ent, sws);
+                         a.targets, a.c, a.beta, a.lp, a.ent, sws, a.root);
       break;
     default:
       return hipErrorInvalidValue;
@@ -441,7 +324,7 @@ hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_shard_merge(sws, a.T, a.targets, a.V, (int64_t)(8 / a.S) * a.Vc, a.c, a.beta,
-                            a.S, a.lp, a.ent, nullptr, stream);
+                            a.S, a.lp, a.ent, a.root, stream);
 }
 
 }  // namespace rlk

@@ -1,0 +1,380 @@
+// Fused path, backward: gradients of sum_r g_lp[r] logprob[r] + g_ent[r] entropy[r] with
+// respect to the hidden states and the LM-head weight, for logits x = H W^T (bf16).
+//
+//   dX[r, v] = ( g_lp[r] (delta(v, t_r) - p_rv) - g_ent[r] p_rv (ln p_rv + H_r) ) / tau
+//   dH = dX W   (contraction over the vocabulary),   dW = dX^T H   (over the tokens).
+// The RL-Kernel h100-pcp.json evidence page's training records consume the logprob and
+// entropy; its comparison block finds the trained weights and norms equal across parallel
+// configurations, which asks for a deterministic gradient with fixed reduction orders.
+//
+// Steps (all on the caller's stream, no atomics):
+//   1. the forward fused path in row-state mode: each token's root state (m, s, u);
+//   2. per-token constants (m, log2 s, entropy, upstream gradients, target, row mode);
+//   3. the logits tile is recomputed on MFMA (same tile loop and K order as the forward)
+//      and its gradient dX is written in bf16, row-major [T, Vp] and transposed [V, Tp];
+//   4. W^T [d, Vp] and H^T [d, Tp] (bf16 transposes, zero padding on K);
+//   5. dH^T = W^T . dX^T as an NT GEMM (both operands K-contiguous), K = Vp split into 8
+//      fixed ranges (boundaries depend on V only), partials summed in the fixed tree
+//      ((0,1),(2,3)),((4,5),(6,7));
+//   6. dW = dX^T . H as an NT GEMM, K = Tp in one increasing-order pass per output tile.
+// A token's row of dH depends only on that token (its place among the GEMM's columns does
+// not change the accumulation order), so dH is batch-invariant like the forward; dW sums
+// over the batch in increasing token order.
+
+#include "rlk_launch.hpp"
+#include "rlk_mma_tile.hpp"
+#include "rlk_state.hpp"
+
+namespace rlk {
+
+namespace {
+
+using mma::floatx16;
+using mma::kBK;
+using mma::kStageBytes;
+using mma::kThreads;
+
+constexpr int kTile = 256;
+constexpr int kDhSplits = 8;
+
+struct GradRowC {
+  float m, lg2s, H, beta, gl, ge;
+  int32_t mode;  // 0 compute, 1 all-zero row, 2 NaN row
+  int32_t pad;
+  int64_t t;
+};
+
+__device__ __forceinline__ uint16_t to_bf16_rne(float f) {
+  const uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // quiet NaN
+  return (uint16_t)((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
+}
+
+__global__ __launch_bounds__(256) void row_consts_kernel(
+    const WireState* __restrict__ root, int64_t T, int64_t V, const int64_t* __restrict__ targets,
+    const float* __restrict__ g_lp, const float* __restrict__ g_ent, double beta,
+    GradRowC* __restrict__ out) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= T) return;
+  GradRowC r;
+  r.gl = g_lp ? g_lp[row] : 0.0f;
+  r.ge = g_ent ? g_ent[row] : 0.0f;
+  r.t = targets ? targets[row] : -1;
+  r.beta = (float)beta;
+  r.m = 0.0f;
+  r.lg2s = 0.0f;
+  r.H = 0.0f;
+  r.pad = 0;
+  if (r.gl == 0.0f && r.ge == 0.0f) {
+    r.mode = 1;
+  } else {
+    const State st = from_wire(root[row]);
+    const bool ok =
+        (st.m != kNegInf) && (st.s > 0.0) && (st.s < __builtin_inf()) && (st.u == st.u);
+    const bool has = (r.t >= 0) && (r.t < V);
+    r.mode = (!ok || (!has && r.gl != 0.0f)) ? 2 : 0;
+    if (r.mode == 0) {
+      r.m = st.m;
+      r.lg2s = (float)log2(st.s);
+      r.H = (float)(log(st.s) - kLn2 * (st.u / st.s));
+    }
+  }
+  out[row] = r;
+}
+
+// Gradient of one logit (same formula and fp32 steps as the logits-path backward).
+__device__ __forceinline__ float logit_grad(float x, bool is_target, const GradRowC& r, float c) {
+  if (r.mode != 0) return r.mode == 1 ? 0.0f : __builtin_nanf("");
+  const float a = (x - r.m) * c;
+  const float q = a - r.lg2s;
+  const float p = exp2_hw(q);
+  const float lnp = q * 0.693147180559945309f;
+  const float ent = mul_zero_wins(p, lnp + r.H);
+  return r.beta * (r.gl * ((is_target ? 1.0f : 0.0f) - p) - r.ge * ent);
+}
+
+// Output tile id -> (row tile, column tile), remapped so that consecutive logical tiles
+// (the column tiles of one row tile) run on the same XCD and share its row slice in L2.
+__device__ __forceinline__ bool tile_of(int64_t n_rt, int64_t n_ct, int64_t& rt, int64_t& ct) {
+  const int64_t nb = n_rt * n_ct;
+  const int64_t per_xcd = (nb + 7) / 8;
+  const int64_t hw = blockIdx.x;
+  const int64_t logical = (hw % 8) * per_xcd + hw / 8;
+  if (logical >= nb) return false;
+  rt = logical / n_ct;
+  ct = logical % n_ct;
+  return true;
+}
+
+// Step 3: logits tile (vocab rows x tokens), then its gradient in bf16.
+__global__ __launch_bounds__(kThreads, 1) void dx_tile_kernel(
+    const uint16_t* __restrict__ H, int64_t ldh, const uint16_t* __restrict__ W, int64_t ldw,
+    int64_t d, int64_t T, int64_t V, float c, const GradRowC* __restrict__ rc,
+    uint16_t* __restrict__ dX, int64_t ldx, uint16_t* __restrict__ dXT, int64_t ldxt) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+  int64_t vt, tt;
+  if (!tile_of((V + kTile - 1) / kTile, (T + kTile - 1) / kTile, vt, tt)) return;
+  const int64_t v_lo = vt * kTile;
+  const int64_t t_lo = tt * kTile;
+  const int n_v = (int)min((int64_t)kTile, V - v_lo);
+  const int n_t = (int)min((int64_t)kTile, T - t_lo);
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+  mma::mma_tile(W + v_lo * ldw, ldw, n_v - 1, H + t_lo * ldh, ldh, n_t - 1, 0, (int)(d / kBK),
+                smem, acc);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wv = wave >> 2, wt = wave & 3;
+  const int frow = lane & 31, fhalf = lane >> 5;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int64_t tok = t_lo + wt * 64 + b * 32 + frow;
+    if (tok >= T) continue;
+    const GradRowC r = rc[tok];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int64_t v0 = v_lo + wv * 128 + a * 32 + 8 * g4 + 4 * fhalf;
+        if (v0 >= V) continue;
+        uint16_t bits[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bits[j] = to_bf16_rne(logit_grad(acc[a][b][4 * g4 + j], v0 + j == r.t, r, c));
+        if (dX) {
+          uint16_t* dst = dX + tok * ldx + v0;
+          if (v0 + 4 <= V) {
+            const uint2 w2 = make_uint2((uint32_t)bits[0] | ((uint32_t)bits[1] << 16),
+                                        (uint32_t)bits[2] | ((uint32_t)bits[3] << 16));
+            *reinterpret_cast<uint2*>(dst) = w2;
+          } else {
+            for (int j = 0; j < 4 && v0 + j < V; ++j) dst[j] = bits[j];
+          }
+        }
+        if (dXT) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (v0 + j < V) dXT[(v0 + j) * ldxt + tok] = bits[j];
+        }
+      }
+    }
+  }
+}
+
+// Step 4: out[c][r] = in[r][c] for r < R, c < C; out[c][r] = 0 for R <= r < Rp.
+__global__ __launch_bounds__(256) void transpose_pad_kernel(
+    const uint16_t* __restrict__ in, int64_t ldin, int64_t R, int64_t C,
+    uint16_t* __restrict__ out, int64_t ldout, int64_t Rp) {
+  __shared__ uint16_t tile[64][66];
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int64_t c0 = (int64_t)blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int rr = 4 * k + ty;
+    const int64_t r = r0 + rr, cc = c0 + tx;
+    tile[rr][tx] = (r < R && cc < C) ? in[r * ldin + cc] : (uint16_t)0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int cl = 4 * k + ty;
+    const int64_t cc = c0 + cl, r = r0 + tx;
+    if (cc < C && r < Rp) out[cc * ldout + r] = tile[tx][cl];
+  }
+}
+
+// Zero columns [c_begin, c_end) of rows [0, rows) of a bf16 matrix (K padding of dX, dX^T).
+__global__ __launch_bounds__(256) void zero_cols_kernel(uint16_t* __restrict__ p, int64_t ld,
+                                                        int64_t rows, int64_t c_begin,
+                                                        int64_t c_end) {
+  const int64_t width = c_end - c_begin;
+  const int64_t n = rows * width;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[(i / width) * ld + c_begin + i % width] = 0;
+}
+
+// Steps 5 and 6: C(m, n) = sum_k A[m, k] B[n, k] over the split's K range, in 256 x 256
+// tiles on the shared MFMA loop.  TRANS: stored at C[n * ldc + m] (4 consecutive m per
+// 16-byte store), else at C[m * ldc + n].  Split s (blockIdx.y) covers K steps
+// [s * steps, (s + 1) * steps) and writes C + s * split_stride; an empty range writes 0.
+template <bool TRANS>
+__global__ __launch_bounds__(kThreads, 1) void nt_gemm_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, int64_t M, const uint16_t* __restrict__ B,
+    int64_t ldb, int64_t N, int64_t K, int64_t steps, float* __restrict__ C, int64_t ldc,
+    int64_t split_stride) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+  int64_t mt, nt;
+  if (!tile_of((M + kTile - 1) / kTile, (N + kTile - 1) / kTile, mt, nt)) return;
+  const int64_t m_lo = mt * kTile, n_lo = nt * kTile;
+  const int64_t k_begin = (int64_t)blockIdx.y * steps * kBK;
+  const int64_t k_end = min(k_begin + steps * kBK, K);
+  const int nk = k_end > k_begin ? (int)((k_end - k_begin) / kBK) : 0;
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+  if (nk > 0)
+    mma::mma_tile(A + m_lo * lda, lda, (int)min((int64_t)kTile, M - m_lo) - 1, B + n_lo * ldb, ldb,
+                  (int)min((int64_t)kTile, N - n_lo) - 1, k_begin, nk, smem, acc);
+  float* __restrict__ Cs = C + (int64_t)blockIdx.y * split_stride;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wv = wave >> 2, wt = wave & 3;
+  const int frow = lane & 31, fhalf = lane >> 5;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int64_t n = n_lo + wt * 64 + b * 32 + frow;
+    if (n >= N) continue;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int64_t m0 = m_lo + wv * 128 + a * 32 + 8 * g4 + 4 * fhalf;
+        if (m0 >= M) continue;
+        if constexpr (TRANS) {
+          float* dst = Cs + n * ldc + m0;
+          if (m0 + 4 <= M) {
+            *reinterpret_cast<float4*>(dst) =
+                make_float4(acc[a][b][4 * g4], acc[a][b][4 * g4 + 1], acc[a][b][4 * g4 + 2],
+                            acc[a][b][4 * g4 + 3]);
+          } else {
+            for (int j = 0; j < 4 && m0 + j < M; ++j) dst[j] = acc[a][b][4 * g4 + j];
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (m0 + j < M) Cs[(m0 + j) * ldc + n] = acc[a][b][4 * g4 + j];
+        }
+      }
+    }
+  }
+}
+
+// out[t, k] = ((P0 + P1) + (P2 + P3)) + ((P4 + P5) + (P6 + P7)), P_s = part + s * stride,
+// part rows of d floats; 4 consecutive k per thread (d is a multiple of 64).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
+                                                            int64_t stride, int64_t T, int64_t d,
+                                                            float* __restrict__ out, int64_t ldo) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // quad index
+  const int64_t nq = T * (d / 4);
+  if (q >= nq) return;
+  const int64_t t = q / (d / 4), k = 4 * (q % (d / 4));
+  float4 v[kDhSplits];
+#pragma unroll
+  for (int s = 0; s < kDhSplits; ++s)
+    v[s] = *reinterpret_cast<const float4*>(part + s * stride + t * d + k);
+  auto add = [](float4 x, float4 y) { return make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w); };
+  const float4 r = add(add(add(v[0], v[1]), add(v[2], v[3])), add(add(v[4], v[5]), add(v[6], v[7])));
+  float* dst = out + t * ldo + k;
+  dst[0] = r.x;
+  dst[1] = r.y;
+  dst[2] = r.z;
+  dst[3] = r.w;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+LinearBackwardWorkspace linear_backward_layout(int64_t T, int64_t V, int64_t d, int S) {
+  LinearBackwardWorkspace L;
+  L.Vp = (V + kBK - 1) / kBK * kBK;
+  L.Tp = (T + kBK - 1) / kBK * kBK;
+  size_t off = align256(linear_workspace_layout(T, V, S).total);
+  L.root = off;
+  off += align256((size_t)T * sizeof(WireState));
+  L.rowc = off;
+  off += align256((size_t)T * sizeof(GradRowC));
+  L.wt = off;
+  off += align256((size_t)d * (size_t)L.Vp * 2);
+  L.ht = off;
+  off += align256((size_t)d * (size_t)L.Tp * 2);
+  L.dx = off;
+  off += align256((size_t)T * (size_t)L.Vp * 2);
+  L.dxt = off;
+  off += align256((size_t)V * (size_t)L.Tp * 2);
+  L.part = off;
+  off += align256((size_t)kDhSplits * (size_t)T * (size_t)d * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_linear_backward(const LinearArgs& fwd, const float* g_lp, const float* g_ent,
+                                  float* dH, int64_t ld_dh, float* dW, int64_t ld_dw,
+                                  hipStream_t stream) {
+  const int64_t T = fwd.T, V = fwd.V, d = fwd.d;
+  const LinearBackwardWorkspace L = linear_backward_layout(T, V, d, fwd.S);
+  char* base = static_cast<char*>(fwd.ws);
+  LinearArgs a = fwd;
+  a.root = reinterpret_cast<WireState*>(base + L.root);
+  a.lp = nullptr;
+  a.ent = nullptr;
+  hipError_t e = launch_linear_path(a, stream);  // step 1
+  if (e != hipSuccess) return e;
+  GradRowC* rc = reinterpret_cast<GradRowC*>(base + L.rowc);
+  hipLaunchKernelGGL(row_consts_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, stream,
+                     a.root, T, V, a.targets, g_lp, g_ent, a.beta, rc);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  uint16_t* wt = reinterpret_cast<uint16_t*>(base + L.wt);
+  uint16_t* ht = reinterpret_cast<uint16_t*>(base + L.ht);
+  uint16_t* dx = dH ? reinterpret_cast<uint16_t*>(base + L.dx) : nullptr;
+  uint16_t* dxt = dW ? reinterpret_cast<uint16_t*>(base + L.dxt) : nullptr;
+  const unsigned fill_blocks = 2048;
+  if (dH) {
+    hipLaunchKernelGGL(transpose_pad_kernel, dim3((unsigned)(L.Vp / 64), (unsigned)(d / 64)),
+                       dim3(256), 0, stream, a.W, a.ldw, V, d, wt, L.Vp, L.Vp);
+    if (L.Vp > V)
+      hipLaunchKernelGGL(zero_cols_kernel, dim3(fill_blocks), dim3(256), 0, stream, dx, L.Vp, T, V,
+                         L.Vp);
+  }
+  if (dW) {
+    hipLaunchKernelGGL(transpose_pad_kernel, dim3((unsigned)(L.Tp / 64), (unsigned)(d / 64)),
+                       dim3(256), 0, stream, a.H, a.ldh, T, d, ht, L.Tp, L.Tp);
+    if (L.Tp > T)
+      hipLaunchKernelGGL(zero_cols_kernel, dim3(fill_blocks), dim3(256), 0, stream, dxt, L.Tp, V,
+                         T, L.Tp);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  const int64_t tiles_x = ((V + kTile - 1) / kTile) * ((T + kTile - 1) / kTile);
+  hipLaunchKernelGGL(dx_tile_kernel, dim3((unsigned)((tiles_x + 7) / 8 * 8)), dim3(kThreads), 0,
+                     stream, a.H, a.ldh, a.W, a.ldw, d, T, V, a.c, rc, dx, L.Vp, dxt, L.Tp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  if (dH) {
+    // dH^T[k, t] = sum_v W^T[k, v] dX[t, v]: A = W^T (M = d), B = dX (N = T), K = Vp.
+    float* part = reinterpret_cast<float*>(base + L.part);
+    const int64_t steps = (L.Vp / kBK + kDhSplits - 1) / kDhSplits;
+    const int64_t tiles = ((d + kTile - 1) / kTile) * ((T + kTile - 1) / kTile);
+    hipLaunchKernelGGL((nt_gemm_kernel<true>), dim3((unsigned)((tiles + 7) / 8 * 8), kDhSplits),
+                       dim3(kThreads), 0, stream, wt, L.Vp, d, dx, L.Vp, T, L.Vp, steps, part, d,
+                       T * d);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t nq = T * (d / 4);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0,
+                       stream, part, T * d, T, d, dH, ld_dh);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (dW) {
+    // dW[v, k] = sum_t dX^T[v, t] H^T[k, t]: A = dX^T (M = V), B = H^T (N = d), K = Tp.
+    const int64_t tiles = ((V + kTile - 1) / kTile) * ((d + kTile - 1) / kTile);
+    hipLaunchKernelGGL((nt_gemm_kernel<false>), dim3((unsigned)((tiles + 7) / 8 * 8), 1),
+                       dim3(kThreads), 0, stream, dxt, L.Tp, V, ht, L.Tp, d, L.Tp,
+                       L.Tp / kBK, dW, ld_dw, (int64_t)0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace rlk

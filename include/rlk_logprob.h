@@ -67,6 +67,7 @@ typedef enum {
 #define RLK_OP_ENTROPY 2
 #define RLK_OP_COMPARE 3
 #define RLK_OP_BACKWARD_FROM_LOGITS 4
+#define RLK_OP_LINEAR_BACKWARD 5
 
 /*
  * Device workspace, in bytes, that the call `op` needs for these sizes.  Pure host
@@ -171,6 +172,37 @@ rlk_status rlk_logprob_backward_from_logits(const float* logits, int64_t ld_logi
                                             const float* grad_entropy, float* grad_logits,
                                             int64_t ld_grad, void* workspace,
                                             size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of the fused path: gradients of  sum_r g_lp[r] logprob[r] + g_ent[r] entropy[r]
+ * with respect to the hidden states and the LM-head weight, for the quantities
+ * rlk_linear_logprob computes (logits x = hidden . weight^T).  With dX the logit gradient of
+ * rlk_logprob_backward_from_logits:   grad_hidden = dX . weight,   grad_weight = dX^T . hidden.
+ * The RL-Kernel h100-pcp.json evidence page's training records consume both outputs and
+ * find the trained weights equal across parallel configurations: the reductions here have
+ * fixed orders (the vocabulary in 8 fixed ranges summed in a fixed tree for grad_hidden,
+ * the tokens in increasing order for grad_weight), with no atomics, so results repeat
+ * bitwise, and each row of grad_hidden is independent of the other rows of the batch.
+ *   hidden, ld_hidden, weight, ld_weight, n_tokens, hidden_dim, vocab, target_ids,
+ *   temperature, vocab_splits: as for rlk_linear_logprob (target_ids may be NULL if
+ *                   grad_logprob is NULL)
+ *   grad_logprob, grad_entropy: [n_tokens] fp32 upstream gradients, or NULL (= 0)
+ *   grad_hidden     [n_tokens, ld_grad_hidden] fp32 output, or NULL (not computed)
+ *   grad_weight     [vocab, ld_grad_weight] fp32 output, or NULL (not computed)
+ *   workspace       rlk_workspace_bytes(RLK_OP_LINEAR_BACKWARD, ...) bytes, 256-aligned
+ * The logit gradient is formed in fp32 and rounded to bf16 for the two bf16 MFMA products
+ * (fp32 accumulation).  Row rules as for rlk_logprob_backward_from_logits; a NaN row of the
+ * logit gradient makes the corresponding grad_hidden row, and every grad_weight entry, NaN.
+ */
+rlk_status rlk_linear_logprob_backward(const uint16_t* hidden_bf16, int64_t ld_hidden,
+                                       const uint16_t* weight_bf16, int64_t ld_weight,
+                                       int64_t n_tokens, int64_t hidden_dim, int64_t vocab,
+                                       const int64_t* target_ids, float temperature,
+                                       int32_t vocab_splits, const float* grad_logprob,
+                                       const float* grad_entropy, float* grad_hidden,
+                                       int64_t ld_grad_hidden, float* grad_weight,
+                                       int64_t ld_grad_weight, void* workspace,
+                                       size_t workspace_bytes, void* stream);
 
 /*
  * Train-vs-rollout selected-logprob comparison over the active tokens: the figures the

@@ -35,7 +35,8 @@ def test_exports_every_header_symbol(L):
     assert set(names) == {"rlk_workspace_bytes", "rlk_logprob_from_logits", "rlk_linear_logprob",
                           "rlk_entropy", "rlk_status_string", "rlk_backend_id",
                           "rlk_logprob_from_logits_bf16", "rlk_entropy_bf16",
-                          "rlk_logprob_compare", "rlk_logprob_backward_from_logits"}
+                          "rlk_logprob_compare", "rlk_logprob_backward_from_logits",
+                          "rlk_linear_logprob_backward"}
     for n in names:
         assert hasattr(L.lib, n), n
         assert ctypes.cast(getattr(L.lib, n), ctypes.c_void_p).value
@@ -184,6 +185,38 @@ def test_backward_validation(L, kw, code):
     assert L.lib.rlk_logprob_backward_from_logits(
         a["logits"], a["ld"], a["T"], a["V"], a["targets"], a["tau"], a["S"], a["glp"],
         a["gent"], a["grad"], a["ldg"], a["ws"], a["wsb"], None) == code
+
+
+def test_linear_backward_workspace_and_validation(L):
+    T, V, d = 2048, 151936, 4096
+    ws = L.workspace_bytes(B.OP_LINEAR_BACKWARD, T, V, d, 1)
+    Vp, Tp = 151936, 2048
+    assert ws >= L.workspace_bytes(B.OP_LINEAR, T, V, d, 1) + d * Vp * 2 + d * Tp * 2 + \
+        2 * T * Vp * 2 + 8 * T * d * 4
+    assert L.workspace_bytes(B.OP_LINEAR_BACKWARD, 0, V, d, 1) == 0
+    with pytest.raises(B.RlkError):
+        L.workspace_bytes(B.OP_LINEAR_BACKWARD, T, V, 100, 1)         # d not a multiple of 64
+    f = L.lib.rlk_linear_logprob_backward
+    base = dict(h=FAKE, ldh=2048, w=FAKE, ldw=2048, T=4, d=2048, V=1000, tg=FAKE, tau=1.0, S=1,
+                glp=FAKE, gent=None, dh=FAKE, lddh=2048, dw=FAKE, lddw=2048, ws=FAKE, wsb=1 << 40)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return f(a["h"], a["ldh"], a["w"], a["ldw"], a["T"], a["d"], a["V"], a["tg"], a["tau"],
+                 a["S"], a["glp"], a["gent"], a["dh"], a["lddh"], a["dw"], a["lddw"], a["ws"],
+                 a["wsb"], None)
+    assert call(d=96) == B.RLK_ERR_INVALID_ARGUMENT
+    assert call(lddh=1000) == B.RLK_ERR_INVALID_ARGUMENT
+    assert call(lddw=1000) == B.RLK_ERR_INVALID_ARGUMENT
+    assert call(tg=None) == B.RLK_ERR_INVALID_ARGUMENT
+    assert call(h=FAKE + 2) == B.RLK_ERR_INVALID_ARGUMENT
+    assert call(wsb=1000) == B.RLK_ERR_WORKSPACE_TOO_SMALL
+    assert call(ws=FAKE + 64) == B.RLK_ERR_INVALID_ARGUMENT
+    assert call(dh=None, dw=None) == B.RLK_OK                      # nothing requested
+    assert call(T=0, h=None, w=None, ws=None, wsb=0) == B.RLK_OK
+    assert call() == B.RLK_ERR_UNSUPPORTED_DEVICE
+    assert call(tg=None, glp=None, gent=FAKE) == B.RLK_ERR_UNSUPPORTED_DEVICE
 
 
 def call_linear(L, h=FAKE, ldh=2048, w=FAKE, ldw=2048, T=4, d=2048, V=1000, tg=FAKE, tau=1.0,

@@ -1,0 +1,147 @@
+"""GPU parity of rlk_linear_logprob_backward (dH = dX W, dW = dX^T H) against the fp64
+oracle, and its strictness: each row of dH bitwise independent of the rest of the batch,
+both gradients bitwise independent of the vocab split and of repeats."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from entropy_rlk_logprob_amd import synthetic as S
+from tests.helpers import announce, bits_dev, bitwise_equal, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def f32(bits):
+    return S.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def run_bwd(lib, h, w, t, tau, split, gl, ge, need_hidden=True, need_weight=True):
+    import torch
+    hd = h if isinstance(h, torch.Tensor) else bits_dev(h)
+    wd = w if isinstance(w, torch.Tensor) else bits_dev(w)
+    td = None if t is None else (t if isinstance(t, torch.Tensor) else dev(np.asarray(t, np.int64)))
+    gld = None if gl is None else (gl if isinstance(gl, torch.Tensor) else dev(gl))
+    ged = None if ge is None else (ge if isinstance(ge, torch.Tensor) else dev(ge))
+    dh, dw = lib.linear_logprob_backward(hd, wd, td, tau, split, gld, ged, need_hidden,
+                                         need_weight)
+    torch.cuda.synchronize()
+    return (None if dh is None else dh.cpu().numpy(), None if dw is None else dw.cpu().numpy())
+
+
+def bound(gx, other, K):
+    """|error| bound of a product dX . other computed from bf16(dX) with fp32 accumulation
+    over K terms: bf16 rounding of dX (2^-9, taken as 2^-8) plus the worst-case fp32
+    accumulation K * 2^-24, both of sum |dX| |other|."""
+    mag = np.abs(gx) @ np.abs(other)
+    return (2.0 ** -8 + K * 2.0 ** -24) * mag + 1e-30
+
+
+def check(gpu, ref, tol):
+    assert np.array_equal(np.isnan(gpu), np.isnan(ref)), "NaN pattern differs"
+    fin = ~np.isnan(ref)
+    err = np.abs(gpu[fin].astype(np.float64) - ref[fin])
+    assert np.all(err <= tol[fin]), (float(err.max()), float((err / tol[fin]).max()))
+
+
+def weights(T, seed):
+    rng = np.random.default_rng(seed)
+    return rng.normal(size=T).astype(np.float32), rng.normal(size=T).astype(np.float32)
+
+
+@pytest.mark.parametrize("T,d,V,tau", [
+    (3, 64, 100, 1.0), (37, 128, 1000, 0.7), (300, 192, 5003, 1.0), (513, 64, 2049, 1.0),
+    (64, 512, 20000, 0.7),
+])
+def test_shapes_vs_oracle_and_split_bitwise(lib, T, d, V, tau):
+    announce(f"linear backward T={T} d={d} V={V} tau={tau}")
+    case = S.random_fused_case(T, d, V, seed=9500 + T + V, h_sigma=1.0,
+                               w_sigma=3.0 / math.sqrt(d), temperature=tau)
+    gl, ge = weights(T, T + V)
+    h, w = f32(case.h_bits), f32(case.w_bits)
+    gx = oracle.logits_grad(h @ w.T, case.targets, tau, gl, ge)
+    ref_dh, ref_dw = gx @ w, gx.T @ h
+    Vp, Tp = -(-V // 64) * 64, -(-T // 64) * 64
+    tol_dh, tol_dw = bound(gx, w, Vp), bound(gx.T, h, Tp)
+    first = None
+    for split in (1, 4):
+        dh, dw = run_bwd(lib, case.h_bits, case.w_bits, case.targets, tau, split, gl, ge)
+        check(dh, ref_dh, tol_dh)
+        check(dw, ref_dw, tol_dw)
+        if first is None:
+            first = (dh, dw)
+        else:
+            assert bitwise_equal(dh, first[0]) and bitwise_equal(dw, first[1]), split
+    # one gradient at a time gives the same bits
+    dh_only, none_w = run_bwd(lib, case.h_bits, case.w_bits, case.targets, tau, 1, gl, ge, True,
+                              False)
+    none_h, dw_only = run_bwd(lib, case.h_bits, case.w_bits, case.targets, tau, 1, gl, ge, False,
+                              True)
+    assert none_w is None and none_h is None
+    assert bitwise_equal(dh_only, first[0]) and bitwise_equal(dw_only, first[1])
+
+
+def test_entropy_only_and_masked_rows(lib):
+    T, d, V = 70, 128, 3001
+    case = S.random_fused_case(T, d, V, seed=96, w_sigma=0.25)
+    rng = np.random.default_rng(97)
+    ge = rng.normal(size=T).astype(np.float32)
+    ge[::5] = 0.0                                   # masked rows (no logprob gradient either)
+    announce("linear backward entropy only, masked rows")
+    h, w = f32(case.h_bits), f32(case.w_bits)
+    gx = oracle.logits_grad(h @ w.T, np.zeros(T, np.int64), 1.0, None, ge)
+    dh, dw = run_bwd(lib, case.h_bits, case.w_bits, None, 1.0, 1, None, ge)
+    check(dh, gx @ w, bound(gx, w, -(-V // 64) * 64))
+    check(dw, gx.T @ h, bound(gx.T, h, -(-T // 64) * 64))
+    assert np.all(dh[::5] == 0.0)
+
+
+def test_rows_of_dh_independent_of_batch(lib):
+    """Sequences of a packed batch alone give the packed rows of dH bitwise."""
+    import torch
+    T, d, V = 640, 256, 20011
+    case = S.random_fused_case(T, d, V, seed=98, w_sigma=3.0 / math.sqrt(d))
+    gl, ge = weights(T, 99)
+    hd, wd, td = bits_dev(case.h_bits), bits_dev(case.w_bits), dev(case.targets)
+    gld, ged = dev(gl), dev(ge)
+    announce("linear backward packed batch")
+    dh, _ = run_bwd(lib, hd, wd, td, 1.0, 1, gld, ged, True, False)
+    for lo, hi in [(0, 1), (1, 129), (129, 600), (600, 640)]:
+        announce(f"linear backward rows [{lo},{hi}) alone")
+        part, _ = run_bwd(lib, hd[lo:hi], wd, td[lo:hi], 1.0, 1, gld[lo:hi], ged[lo:hi], True,
+                          False)
+        assert bitwise_equal(part, dh[lo:hi]), (lo, hi)
+    perm = torch.from_numpy(np.random.default_rng(100).permutation(T)).cuda()
+    dhp, _ = run_bwd(lib, hd[perm].contiguous(), wd, td[perm].contiguous(), 1.0, 1,
+                     gld[perm].contiguous(), ged[perm].contiguous(), True, False)
+    assert bitwise_equal(dhp, dh[perm.cpu().numpy()])
+
+
+def test_qwen3_vocab_full_hidden_vs_oracle(lib):
+    """V = 151936, d = 4096, T = 256 (several token tiles of work per vocabulary tile):
+    sampled rows of dH and sampled vocabulary rows of dW against the oracle; repeats bitwise."""
+    T, d, V = 256, 4096, 151936
+    announce("generating linear backward case T=256 d=4096 V=151936")
+    case = S.random_fused_case(T, d, V, seed=101, h_sigma=1.0, w_sigma=0.02)
+    gl, ge = weights(T, 102)
+    hd, wd, td = bits_dev(case.h_bits), bits_dev(case.w_bits), dev(case.targets)
+    gld, ged = dev(gl), dev(ge)
+    announce("linear backward T=256 d=4096 V=151936")
+    dh, dw = run_bwd(lib, hd, wd, td, 1.0, 1, gld, ged)
+    h = f32(case.h_bits)
+    w = f32(case.w_bits)
+    gx = np.empty((T, V))
+    for lo in range(0, T, 32):                       # row blocks keep the fp64 logits small
+        gx[lo:lo + 32] = oracle.logits_grad(h[lo:lo + 32] @ w.T, case.targets[lo:lo + 32], 1.0,
+                                            gl[lo:lo + 32], ge[lo:lo + 32])
+    rows = np.array([0, 1, 77, 128, 255])
+    check(dh[rows], gx[rows] @ w, bound(gx[rows], w, V))
+    vrows = np.unique(np.concatenate([[0, 1, 255, 256, 18991, 18992, 151935],
+                                      np.random.default_rng(103).integers(0, V, 20)]))
+    check(dw[vrows], gx[:, vrows].T @ h, bound(gx[:, vrows].T, h, T))
+    announce("linear backward T=256 repeat and split 8")
+    dh2, dw2 = run_bwd(lib, hd, wd, td, 1.0, 8, gld, ged)
+    assert bitwise_equal(dh2, dh) and bitwise_equal(dw2, dw)
