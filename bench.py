@@ -19,7 +19,9 @@ Also reported on the same JSON line:
                 (1024 x 303888 B per call) as GB/s against 8 TB/s;
   backward      rlk_logprob_backward_from_logits on the same rows (gradient of
                 g_lp * logprob + g_ent * entropy): ms per call and GB/s over its
-                algorithmic bytes (one read of the logits, one write of the gradient).
+                algorithmic bytes (one read of the logits, one write of the gradient);
+  fused_backward  rlk_linear_logprob_backward on the Qwen3-8B shape: ms per call and
+                TFLOP/s over 3 x 2 T V d flops (logits, dH, dW) vs the bf16 peak.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--no-fused]
 """
@@ -171,11 +173,18 @@ def main():
     gout = torch.empty_like(x)
     bw_ws = torch.empty(max(1, lib.workspace_bytes(binding.OP_BACKWARD_FROM_LOGITS, T, V, 0, 1)),
                         dtype=torch.uint8, device="cuda")
+    states = lib.row_states_buffer(T)
+    lib.logprob_from_logits(x, t, 1.0, 1, out=(lp, ent), row_states=states)
     g_ms, g_wall = time_calls(lambda: lib.logprob_backward_from_logits(
-        x, t, 1.0, 1, gl, ge, out=gout, workspace=bw_ws), max(5, args.steps // 2), 5)
+        x, t, 1.0, 1, gl, ge, out=gout, workspace=bw_ws, row_states=states),
+        max(5, args.steps // 2), 5)
+    g_ms_re, _ = time_calls(lambda: lib.logprob_backward_from_logits(
+        x, t, 1.0, 1, gl, ge, out=gout, workspace=bw_ws), max(5, args.steps // 4), 3)
     g_gbs = T * BYTES_PER_TOKEN_BACKWARD / (g_ms / 1e3) / 1e9
     backward = {"ms_per_call": round(g_ms, 5), "tokens_per_s": round(T / (g_wall / 1e3), 1),
-                "kernels": "row_reduce_kernel (row states) + logits_grad_kernel",
+                "row_states": "saved by the forward call",
+                "ms_per_call_recomputing_row_states": round(g_ms_re, 5),
+                "kernels": "logits_grad_kernel (+ row_reduce_kernel when recomputing)",
                 "roofline": {"bound": "hbm", "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": round(g_gbs / HBM_PEAK_GBS, 4),
                              "algorithmic_bytes": T * BYTES_PER_TOKEN_BACKWARD}}
@@ -197,6 +206,7 @@ def main():
     del xh
 
     fused = None
+    fused_backward = None
     if not args.no_fused:
         log("generating fused workload T=2048 d=4096 V=151936 (bf16)")
         fc = S.fused_workload(4)
@@ -215,6 +225,34 @@ def main():
         fsteps = max(5, min(args.steps, 20))
         log(f"timing fused path: steps {fsteps}")
         f_ms, f_wall = time_calls(fstep, fsteps, 3)
+        log("timing fused backward")
+        fgl = torch.randn(Tf, generator=torch.Generator().manual_seed(9)).cuda()
+        fge = torch.randn(Tf, generator=torch.Generator().manual_seed(10)).cuda()
+        fdh = torch.empty((Tf, d), dtype=torch.float32, device="cuda")
+        fdw = torch.empty((V, d), dtype=torch.float32, device="cuda")
+        fbws = torch.empty(lib.workspace_bytes(binding.OP_LINEAR_BACKWARD, Tf, V, d, 1),
+                           dtype=torch.uint8, device="cuda")
+
+        fstates = lib.row_states_buffer(Tf)
+        lib.linear_logprob(h, w, tt, 1.0, 1, out=(flp, fent), workspace=fws, row_states=fstates)
+
+        def bstep(states=fstates):
+            lib.linear_logprob_backward(h, w, tt, 1.0, 1, fgl, fge, out=(fdh, fdw),
+                                        workspace=fbws, row_states=states)
+
+        b_ms_f, b_wall_f = time_calls(bstep, max(3, min(args.steps, 10)), 2)
+        b_ms_re, _ = time_calls(lambda: bstep(None), 3, 1)
+        bflops = 3 * 2.0 * Tf * V * d
+        btf = bflops / (b_ms_f / 1e3) / 1e12
+        fused_backward = {"ms_per_call": round(b_ms_f, 4),
+                          "tokens_per_s": round(Tf / (b_wall_f / 1e3), 1),
+                          "row_states": "saved by the forward call",
+                          "ms_per_call_recomputing_row_states": round(b_ms_re, 4),
+                          "roofline": {"bound": "mfma", "achieved": round(btf, 1),
+                                       "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": round(btf / BF16_PEAK_TFLOPS, 4),
+                                       "flops_per_call": bflops}}
+        del fdh, fdw, fbws
         flops = 2.0 * Tf * V * d
         tflops = flops / (f_ms / 1e3) / 1e12
         fused = {"workload": S.WORKLOADS[4].name, "n_tokens": Tf, "hidden": d, "vocab": V,
@@ -236,7 +274,7 @@ def main():
                    "vocab_splits": 1, "temperature": 1.0, "logits_dtype": "f32",
                    "parallelism": "single-gpu"},
         "backend": lib.backend_id(),
-        "roofline": roofline, "cpu_baseline": cpu, "fused": fused, "splits_ms": splits,
+        "roofline": roofline, "cpu_baseline": cpu, "fused": fused, "fused_backward": fused_backward, "splits_ms": splits,
         "bf16_logits": bf16, "backward": backward,
         "device": torch.cuda.get_device_name(0),
     }

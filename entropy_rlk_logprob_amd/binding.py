@@ -24,6 +24,7 @@ RLK_ERR_HIP = 4
 
 OP_FROM_LOGITS, OP_LINEAR, OP_ENTROPY, OP_COMPARE, OP_BACKWARD_FROM_LOGITS = 0, 1, 2, 3, 4
 OP_LINEAR_BACKWARD = 5
+ROW_STATE_BYTES = 24   # sizeof(rlk_row_state)
 
 # Field order of rlk_compare_result (8 x 8 bytes: four int64, then four double).
 COMPARE_FIELDS = ("active_tokens", "mismatch_count", "bitwise_mismatch_count", "reserved",
@@ -69,17 +70,19 @@ class Library:
                                           ctypes.POINTER(ctypes.c_size_t)]
         L.rlk_logprob_from_logits.restype = ctypes.c_int
         L.rlk_logprob_from_logits.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_float,
-                                              ctypes.c_int32, _c_p, _c_p, _c_p, ctypes.c_size_t,
-                                              _c_p]
+                                              ctypes.c_int32, _c_p, _c_p, _c_p, _c_p,
+                                              ctypes.c_size_t, _c_p]
         L.rlk_linear_logprob.restype = ctypes.c_int
         L.rlk_linear_logprob.argtypes = [_c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p,
-                                         ctypes.c_float, ctypes.c_int32, _c_p, _c_p, _c_p,
+                                         ctypes.c_float, ctypes.c_int32, _c_p, _c_p, _c_p, _c_p,
                                          ctypes.c_size_t, _c_p]
         L.rlk_entropy.restype = ctypes.c_int
         L.rlk_entropy.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, ctypes.c_float, ctypes.c_int32,
                                   _c_p, _c_p, ctypes.c_size_t, _c_p]
         L.rlk_logprob_from_logits_bf16.restype = ctypes.c_int
-        L.rlk_logprob_from_logits_bf16.argtypes = L.rlk_logprob_from_logits.argtypes
+        L.rlk_logprob_from_logits_bf16.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, _c_p,
+                                                   ctypes.c_float, ctypes.c_int32, _c_p, _c_p,
+                                                   _c_p, ctypes.c_size_t, _c_p]
         L.rlk_entropy_bf16.restype = ctypes.c_int
         L.rlk_entropy_bf16.argtypes = L.rlk_entropy.argtypes
         L.rlk_logprob_compare.restype = ctypes.c_int
@@ -88,11 +91,12 @@ class Library:
         L.rlk_logprob_backward_from_logits.restype = ctypes.c_int
         L.rlk_logprob_backward_from_logits.argtypes = [
             _c_p, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_float, ctypes.c_int32, _c_p, _c_p, _c_p,
-            _c_i64, _c_p, ctypes.c_size_t, _c_p]
+            _c_p, _c_i64, _c_p, ctypes.c_size_t, _c_p]
         L.rlk_linear_logprob_backward.restype = ctypes.c_int
         L.rlk_linear_logprob_backward.argtypes = [
             _c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_float,
-            ctypes.c_int32, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64, _c_p, ctypes.c_size_t, _c_p]
+            ctypes.c_int32, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i64, _c_p, ctypes.c_size_t,
+            _c_p]
         L.rlk_status_string.restype = ctypes.c_char_p
         L.rlk_status_string.argtypes = [ctypes.c_int]
         L.rlk_backend_id.restype = ctypes.c_char_p
@@ -146,14 +150,27 @@ class Library:
         return ws, nbytes
 
     @staticmethod
+    def row_states_buffer(n_tokens: int, device="cuda"):
+        """Storage for n_tokens rlk_row_state records (24 bytes each)."""
+        import torch
+        return torch.empty(max(1, n_tokens) * ROW_STATE_BYTES, dtype=torch.uint8, device=device)
+
+    @staticmethod
+    def _check_states(states, T: int):
+        if states is not None:
+            assert states.is_contiguous() and states.numel() * states.element_size() >= T * 24
+            assert states.data_ptr() % 8 == 0
+
+    @staticmethod
     def _ptr(t) -> int | None:
         return None if t is None else t.data_ptr()
 
     def logprob_from_logits(self, logits, targets, temperature: float = 1.0,
                             vocab_splits: int = 1, with_entropy: bool = True, out=None,
-                            workspace=None, stream=None):
+                            workspace=None, stream=None, row_states=None):
         """logits: [T, >=V] float32 or bfloat16 CUDA tensor (row stride = ld);
-        targets: [T] int64."""
+        targets: [T] int64; row_states: optional [T * 24] uint8 tensor (fp32 logits only)
+        that receives the rows' states for the backward call."""
         import torch
         assert logits.dtype in (torch.float32, torch.bfloat16)
         assert logits.dim() == 2 and logits.stride(1) == 1
@@ -165,12 +182,18 @@ class Library:
             torch.empty(T, dtype=torch.float32, device=dev) if with_entropy else None)
         ws, wsb = self._workspace(self.workspace_bytes(OP_FROM_LOGITS, T, V, 0, vocab_splits),
                                   dev, workspace)
-        fn = (self.lib.rlk_logprob_from_logits if logits.dtype == torch.float32
-              else self.lib.rlk_logprob_from_logits_bf16)
-        st = fn(
-            self._ptr(logits), logits.stride(0), T, V, self._ptr(targets), temperature,
-            vocab_splits, self._ptr(lp), self._ptr(ent), self._ptr(ws), wsb,
-            self._stream_handle(stream))
+        if logits.dtype == torch.float32:
+            self._check_states(row_states, T)
+            st = self.lib.rlk_logprob_from_logits(
+                self._ptr(logits), logits.stride(0), T, V, self._ptr(targets), temperature,
+                vocab_splits, self._ptr(lp), self._ptr(ent), self._ptr(row_states),
+                self._ptr(ws), wsb, self._stream_handle(stream))
+        else:
+            assert row_states is None, "row states are saved by the fp32 logits call only"
+            st = self.lib.rlk_logprob_from_logits_bf16(
+                self._ptr(logits), logits.stride(0), T, V, self._ptr(targets), temperature,
+                vocab_splits, self._ptr(lp), self._ptr(ent), self._ptr(ws), wsb,
+                self._stream_handle(stream))
         self.check(st, "rlk_logprob_from_logits")
         return lp, ent
 
@@ -193,7 +216,7 @@ class Library:
 
     def linear_logprob(self, hidden, weight, targets, temperature: float = 1.0,
                        vocab_splits: int = 1, with_entropy: bool = True, out=None,
-                       workspace=None, stream=None):
+                       workspace=None, stream=None, row_states=None):
         """hidden: [T, d] bf16 (or int16/uint16 bits); weight: [V, d] same; targets [T] int64."""
         import torch
         assert hidden.dim() == 2 and weight.dim() == 2
@@ -209,17 +232,18 @@ class Library:
             torch.empty(T, dtype=torch.float32, device=dev) if with_entropy else None)
         ws, wsb = self._workspace(self.workspace_bytes(OP_LINEAR, T, V, d, vocab_splits), dev,
                                   workspace)
+        self._check_states(row_states, T)
         st = self.lib.rlk_linear_logprob(
             self._ptr(hidden), hidden.stride(0), self._ptr(weight), weight.stride(0), T, d, V,
             self._ptr(targets), temperature, vocab_splits, self._ptr(lp), self._ptr(ent),
-            self._ptr(ws), wsb, self._stream_handle(stream))
+            self._ptr(row_states), self._ptr(ws), wsb, self._stream_handle(stream))
         self.check(st, "rlk_linear_logprob")
         return lp, ent
 
 
     def logprob_backward_from_logits(self, logits, targets, temperature: float = 1.0,
                                      vocab_splits: int = 1, grad_logprob=None, grad_entropy=None,
-                                     out=None, workspace=None, stream=None):
+                                     out=None, workspace=None, stream=None, row_states=None):
         """Gradient of sum g_lp * logprob + g_ent * entropy w.r.t. fp32 logits [T, >=V];
         returns `out` (new [T, V] fp32 tensor if None; may be `logits` itself)."""
         import torch
@@ -233,19 +257,21 @@ class Library:
         grad = out if out is not None else torch.empty((T, V), dtype=torch.float32,
                                                        device=logits.device)
         assert grad.dtype == torch.float32 and grad.stride(1) == 1 and grad.shape == (T, V)
+        self._check_states(row_states, T)
         ws, wsb = self._workspace(self.workspace_bytes(OP_BACKWARD_FROM_LOGITS, T, V, 0,
                                                        vocab_splits), logits.device, workspace)
         st = self.lib.rlk_logprob_backward_from_logits(
             self._ptr(logits), logits.stride(0), T, V, self._ptr(targets), temperature,
-            vocab_splits, self._ptr(grad_logprob), self._ptr(grad_entropy), self._ptr(grad),
-            grad.stride(0), self._ptr(ws), wsb, self._stream_handle(stream))
+            vocab_splits, self._ptr(grad_logprob), self._ptr(grad_entropy),
+            self._ptr(row_states), self._ptr(grad), grad.stride(0), self._ptr(ws), wsb,
+            self._stream_handle(stream))
         self.check(st, "rlk_logprob_backward_from_logits")
         return grad
 
     def linear_logprob_backward(self, hidden, weight, targets, temperature: float = 1.0,
                                 vocab_splits: int = 1, grad_logprob=None, grad_entropy=None,
                                 need_hidden: bool = True, need_weight: bool = True, out=None,
-                                workspace=None, stream=None):
+                                workspace=None, stream=None, row_states=None):
         """Gradients (dH [T, d], dW [V, d], fp32; None where not requested) of
         sum g_lp * logprob + g_ent * entropy for logits = hidden @ weight^T (bf16 bits)."""
         import torch
@@ -264,12 +290,14 @@ class Library:
         else:
             dh = torch.empty((T, d), dtype=torch.float32, device=dev) if need_hidden else None
             dw = torch.empty((V, d), dtype=torch.float32, device=dev) if need_weight else None
+        self._check_states(row_states, T)
         ws, wsb = self._workspace(self.workspace_bytes(OP_LINEAR_BACKWARD, T, V, d, vocab_splits),
                                   dev, workspace)
         st = self.lib.rlk_linear_logprob_backward(
             self._ptr(hidden), hidden.stride(0), self._ptr(weight), weight.stride(0), T, d, V,
             self._ptr(targets), temperature, vocab_splits, self._ptr(grad_logprob),
-            self._ptr(grad_entropy), self._ptr(dh), dh.stride(0) if dh is not None else 0,
+            self._ptr(grad_entropy), self._ptr(row_states), self._ptr(dh),
+            dh.stride(0) if dh is not None else 0,
             self._ptr(dw), dw.stride(0) if dw is not None else 0, self._ptr(ws), wsb,
             self._stream_handle(stream))
         self.check(st, "rlk_linear_logprob_backward")

@@ -15,6 +15,10 @@
 
 namespace {
 
+static_assert(sizeof(rlk_row_state) == sizeof(rlk::WireState) &&
+                  alignof(rlk_row_state) == alignof(rlk::WireState),
+              "rlk_row_state is the wire state");
+
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
@@ -82,7 +86,7 @@ rlk_status validate_logits(const void* logits, int64_t ld, int64_t T, int64_t V,
 // logits_f32 or logits_bf16 (exactly one non-null) in the same [T, ld] row-major layout.
 rlk_status run_logits(const float* logits_f32, const uint16_t* logits_bf16, int64_t ld, int64_t T,
                       int64_t V, const int64_t* targets, float temperature, int32_t S, float* lp,
-                      float* ent, void* ws, void* stream) {
+                      float* ent, rlk_row_state* states, void* ws, void* stream) {
   rlk::LogitsArgs a;
   a.X = logits_f32;
   a.Xh = logits_bf16;
@@ -99,7 +103,7 @@ rlk_status run_logits(const float* logits_f32, const uint16_t* logits_bf16, int6
   a.lp = lp;
   a.ent = ent;
   a.ws = static_cast<rlk::WireState*>(ws);
-  a.root = nullptr;
+  a.root = reinterpret_cast<rlk::WireState*>(states);
   const hipError_t e = rlk::launch_logits_path(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RLK_OK : RLK_ERR_HIP;
 }
@@ -149,7 +153,8 @@ rlk_status rlk_workspace_bytes(int op, int64_t n_tokens, int64_t vocab, int64_t 
 rlk_status rlk_logprob_from_logits(const float* logits, int64_t ld_logits, int64_t n_tokens,
                                    int64_t vocab, const int64_t* target_ids, float temperature,
                                    int32_t vocab_splits, float* logprob_out, float* entropy_out,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
+                                   rlk_row_state* row_states_out, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
   if (n_tokens > 0 && (!target_ids || !logprob_out)) return RLK_ERR_INVALID_ARGUMENT;
   rlk_status s = validate_logits(logits, ld_logits, n_tokens, vocab, temperature, vocab_splits,
                                  workspace, workspace_bytes);
@@ -157,8 +162,9 @@ rlk_status rlk_logprob_from_logits(const float* logits, int64_t ld_logits, int64
   if (n_tokens == 0) return RLK_OK;
   s = check_device();
   if (s != RLK_OK) return s;
+  if (row_states_out && !aligned(row_states_out, 8)) return RLK_ERR_INVALID_ARGUMENT;
   return run_logits(logits, nullptr, ld_logits, n_tokens, vocab, target_ids, temperature,
-                    vocab_splits, logprob_out, entropy_out, workspace, stream);
+                    vocab_splits, logprob_out, entropy_out, row_states_out, workspace, stream);
 }
 
 rlk_status rlk_logprob_from_logits_bf16(const uint16_t* logits, int64_t ld_logits,
@@ -175,7 +181,7 @@ rlk_status rlk_logprob_from_logits_bf16(const uint16_t* logits, int64_t ld_logit
   s = check_device();
   if (s != RLK_OK) return s;
   return run_logits(nullptr, logits, ld_logits, n_tokens, vocab, target_ids, temperature,
-                    vocab_splits, logprob_out, entropy_out, workspace, stream);
+                    vocab_splits, logprob_out, entropy_out, nullptr, workspace, stream);
 }
 
 rlk_status rlk_entropy_bf16(const uint16_t* logits, int64_t ld_logits, int64_t n_tokens,
@@ -190,7 +196,7 @@ rlk_status rlk_entropy_bf16(const uint16_t* logits, int64_t ld_logits, int64_t n
   s = check_device();
   if (s != RLK_OK) return s;
   return run_logits(nullptr, logits, ld_logits, n_tokens, vocab, nullptr, temperature,
-                    vocab_splits, nullptr, entropy_out, workspace, stream);
+                    vocab_splits, nullptr, entropy_out, nullptr, workspace, stream);
 }
 
 rlk_status rlk_entropy(const float* logits, int64_t ld_logits, int64_t n_tokens, int64_t vocab,
@@ -204,15 +210,15 @@ rlk_status rlk_entropy(const float* logits, int64_t ld_logits, int64_t n_tokens,
   s = check_device();
   if (s != RLK_OK) return s;
   return run_logits(logits, nullptr, ld_logits, n_tokens, vocab, nullptr, temperature,
-                    vocab_splits, nullptr, entropy_out, workspace, stream);
+                    vocab_splits, nullptr, entropy_out, nullptr, workspace, stream);
 }
 
 rlk_status rlk_linear_logprob(const uint16_t* hidden_bf16, int64_t ld_hidden,
                               const uint16_t* weight_bf16, int64_t ld_weight, int64_t n_tokens,
                               int64_t hidden_dim, int64_t vocab, const int64_t* target_ids,
                               float temperature, int32_t vocab_splits, float* logprob_out,
-                              float* entropy_out, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+                              float* entropy_out, rlk_row_state* row_states_out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   if (n_tokens < 0 || n_tokens > kMaxRows || vocab < 1 || vocab > kMaxVocabLinear)
     return RLK_ERR_INVALID_ARGUMENT;
   if (hidden_dim < 64 || hidden_dim > kMaxHidden || hidden_dim % 64 != 0)
@@ -225,6 +231,7 @@ rlk_status rlk_linear_logprob(const uint16_t* hidden_bf16, int64_t ld_hidden,
   if (n_tokens > 0) {
     if (!hidden_bf16 || !weight_bf16 || !target_ids || !logprob_out)
       return RLK_ERR_INVALID_ARGUMENT;
+    if (row_states_out && !aligned(row_states_out, 8)) return RLK_ERR_INVALID_ARGUMENT;
     if (!aligned(hidden_bf16, 16) || !aligned(weight_bf16, 16)) return RLK_ERR_INVALID_ARGUMENT;
     const size_t need = rlk::linear_workspace_layout(n_tokens, vocab, vocab_splits).total;
     if (workspace && !aligned(workspace, 256)) return RLK_ERR_INVALID_ARGUMENT;
@@ -249,7 +256,7 @@ rlk_status rlk_linear_logprob(const uint16_t* hidden_bf16, int64_t ld_hidden,
   a.lp = logprob_out;
   a.ent = entropy_out;
   a.ws = workspace;
-  a.root = nullptr;
+  a.root = reinterpret_cast<rlk::WireState*>(row_states_out);
   const hipError_t e = rlk::launch_linear_path(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RLK_OK : RLK_ERR_HIP;
 }
@@ -291,7 +298,8 @@ rlk_status rlk_logprob_backward_from_logits(const float* logits, int64_t ld_logi
                                             int64_t n_tokens, int64_t vocab,
                                             const int64_t* target_ids, float temperature,
                                             int32_t vocab_splits, const float* grad_logprob,
-                                            const float* grad_entropy, float* grad_logits,
+                                            const float* grad_entropy,
+                                            const rlk_row_state* row_states, float* grad_logits,
                                             int64_t ld_grad, void* workspace,
                                             size_t workspace_bytes, void* stream) {
   if (n_tokens < 0 || n_tokens > kMaxRows || vocab < 1 || vocab > kMaxVocab || ld_logits < vocab ||
@@ -300,6 +308,7 @@ rlk_status rlk_logprob_backward_from_logits(const float* logits, int64_t ld_logi
   if (n_tokens > 0 && (!logits || !grad_logits || (grad_logprob && !target_ids)))
     return RLK_ERR_INVALID_ARGUMENT;
   if (grad_logits == logits && ld_grad != ld_logits) return RLK_ERR_INVALID_ARGUMENT;
+  if (row_states && !aligned(row_states, 8)) return RLK_ERR_INVALID_ARGUMENT;
   if (!valid_temperature(temperature) || !valid_splits(vocab_splits))
     return RLK_ERR_INVALID_ARGUMENT;
   const size_t need = backward_ws_bytes(n_tokens, vocab_splits);
@@ -327,10 +336,13 @@ rlk_status rlk_logprob_backward_from_logits(const float* logits, int64_t ld_logi
   a.ent = nullptr;
   char* ws = static_cast<char*>(workspace);
   a.ws = reinterpret_cast<rlk::WireState*>(ws);
-  a.root = reinterpret_cast<rlk::WireState*>(ws + backward_root_offset(n_tokens, vocab_splits));
+  a.root = row_states ? reinterpret_cast<rlk::WireState*>(const_cast<rlk_row_state*>(row_states))
+                      : reinterpret_cast<rlk::WireState*>(ws + backward_root_offset(n_tokens,
+                                                                                   vocab_splits));
   const bool vec = a.vec && aligned(grad_logits, 16) && ld_grad % 4 == 0;
-  const hipError_t e = rlk::launch_logits_backward(a, grad_logprob, grad_entropy, grad_logits,
-                                                   ld_grad, vec, static_cast<hipStream_t>(stream));
+  const hipError_t e =
+      rlk::launch_logits_backward(a, grad_logprob, grad_entropy, grad_logits, ld_grad, vec,
+                                  row_states != nullptr, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RLK_OK : RLK_ERR_HIP;
 }
 
@@ -339,7 +351,8 @@ rlk_status rlk_linear_logprob_backward(const uint16_t* hidden_bf16, int64_t ld_h
                                        int64_t n_tokens, int64_t hidden_dim, int64_t vocab,
                                        const int64_t* target_ids, float temperature,
                                        int32_t vocab_splits, const float* grad_logprob,
-                                       const float* grad_entropy, float* grad_hidden,
+                                       const float* grad_entropy,
+                                       const rlk_row_state* row_states, float* grad_hidden,
                                        int64_t ld_grad_hidden, float* grad_weight,
                                        int64_t ld_grad_weight, void* workspace,
                                        size_t workspace_bytes, void* stream) {
@@ -357,6 +370,7 @@ rlk_status rlk_linear_logprob_backward(const uint16_t* hidden_bf16, int64_t ld_h
   if (n_tokens > 0) {
     if (!hidden_bf16 || !weight_bf16 || (grad_logprob && !target_ids))
       return RLK_ERR_INVALID_ARGUMENT;
+    if (row_states && !aligned(row_states, 8)) return RLK_ERR_INVALID_ARGUMENT;
     if (!aligned(hidden_bf16, 16) || !aligned(weight_bf16, 16)) return RLK_ERR_INVALID_ARGUMENT;
     const size_t need =
         rlk::linear_backward_layout(n_tokens, vocab, hidden_dim, vocab_splits).total;
@@ -385,7 +399,9 @@ rlk_status rlk_linear_logprob_backward(const uint16_t* hidden_bf16, int64_t ld_h
   a.root = nullptr;
   const hipError_t e =
       rlk::launch_linear_backward(a, grad_logprob, grad_entropy, grad_hidden, ld_grad_hidden,
-                                  grad_weight, ld_grad_weight, static_cast<hipStream_t>(stream));
+                                  grad_weight, ld_grad_weight,
+                                  reinterpret_cast<const rlk::WireState*>(row_states),
+                                  static_cast<hipStream_t>(stream));
   return e == hipSuccess ? RLK_OK : RLK_ERR_HIP;
 }
 

@@ -8,7 +8,7 @@
 // configurations ask for a deterministic gradient).
 //
 // Pass 1 is the forward row reducer (canonical order, any vocab split) writing each row's
-// root state (m, s, u).  Pass 2, below, streams the row again: per element
+// root state (m, s, u) -- skipped when the caller passes the states its forward call saved.  Pass 2, below, streams the row again: per element
 //   a = c (x - m)          (fp32, as in the forward leaf),   q = a - log2 s,
 //   p = 2^q,  ln p = q ln 2,
 //   grad = beta (g_lp (delta_it - p) - g_ent p (ln p + H)),
@@ -114,9 +114,12 @@ __global__ __launch_bounds__(kGradThreads) void logits_grad_kernel(
 }  // namespace
 
 hipError_t launch_logits_backward(const LogitsArgs& a, const float* g_lp, const float* g_ent,
-                                  float* G, int64_t ldg, bool vec, hipStream_t stream) {
-  hipError_t e = launch_logits_path(a, stream);  // a.root receives the row states
-  if (e != hipSuccess) return e;
+                                  float* G, int64_t ldg, bool vec, bool have_states,
+                                  hipStream_t stream) {
+  if (!have_states) {
+    hipError_t e = launch_logits_path(a, stream);  // a.root receives the row states
+    if (e != hipSuccess) return e;
+  }
   const int64_t spans = (a.V + kGradColsPerBlock - 1) / kGradColsPerBlock;
   const dim3 grid((unsigned)a.T, (unsigned)(spans < 4096 ? spans : 4096));
   if (vec)

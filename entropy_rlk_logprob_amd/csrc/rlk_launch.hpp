@@ -29,7 +29,7 @@ struct LogitsArgs {
   float* lp;               // may be null
   float* ent;              // may be null
   WireState* ws;           // S * T wire states when S > 1
-  WireState* root;         // when non-null: each row's root state instead of lp / ent
+  WireState* root;         // when non-null: each row's root state (as well as lp / ent)
 };
 
 hipError_t launch_logits_path(const LogitsArgs& a, hipStream_t stream);
@@ -37,10 +37,12 @@ hipError_t launch_logits_path(const LogitsArgs& a, hipStream_t stream);
 // Backward of the logits path (rlk_backward.hip): the row states into a.root (which must be
 // set), then the gradient G[T, ldg]; vec: 16-byte accesses legal for both X and G.
 hipError_t launch_logits_backward(const LogitsArgs& a, const float* g_lp, const float* g_ent,
-                                  float* G, int64_t ldg, bool vec, hipStream_t stream);
+                                  float* G, int64_t ldg, bool vec, bool have_states,
+                                  hipStream_t stream);
 
 // Top log2(S) levels of the chunk tree over S shard states ([S][T] wire states), then
-// the fp64 finalize of every row (or, when root is non-null, each row's root state).
+// the fp64 finalize of every row (when lp or ent is non-null) and / or each row's root
+// state (when root is non-null).
 // Shared by both paths.
 hipError_t launch_shard_merge(const WireState* ws, int64_t T, const int64_t* targets, int64_t V,
                               int64_t shard_cols, float c, double beta, int S, float* lp,
@@ -57,7 +59,7 @@ struct LinearArgs {
   float* lp;
   float* ent;
   void* ws;  // tile states, target logits, shard states
-  WireState* root;  // when non-null: each token's root state instead of lp / ent
+  WireState* root;  // when non-null: each token's root state (as well as lp / ent)
 };
 
 // Workspace layout of the fused path (offsets in bytes from the workspace base).
@@ -91,9 +93,10 @@ struct LinearBackwardWorkspace {
 LinearBackwardWorkspace linear_backward_layout(int64_t T, int64_t V, int64_t d, int S);
 
 // dH [T, ld_dh] and / or dW [V, ld_dw] (either may be null); a.ws holds the workspace.
+// When states is non-null it holds the forward's row states and the recompute is skipped.
 hipError_t launch_linear_backward(const LinearArgs& a, const float* g_lp, const float* g_ent,
                                   float* dH, int64_t ld_dh, float* dW, int64_t ld_dw,
-                                  hipStream_t stream);
+                                  const WireState* states, hipStream_t stream);
 
 // Train-vs-rollout comparison (rlk_compare.hip).
 using CompareResult = rlk_compare_result;

@@ -241,9 +241,8 @@ __global__ __launch_bounds__(64 * CPS) void tile_tree_kernel(
   if constexpr (CPS == 8) {
     const bool has = (t >= 0) && (t < g.V);
     const float xt = has ? target_logit[tok] : 0.0f;
-    if (root)
-      root[tok] = to_wire(top_state, xt);
-    else
+    if (root) root[tok] = to_wire(top_state, xt);
+    if (lp_out || ent_out)
       rlk_finalize(top_state, xt, has, beta, lp_out ? lp_out + tok : nullptr,
                    ent_out ? ent_out + tok : nullptr);
   } else {

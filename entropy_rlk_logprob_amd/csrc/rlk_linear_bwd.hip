@@ -8,7 +8,8 @@
 // configurations, which asks for a deterministic gradient with fixed reduction orders.
 //
 // Steps (all on the caller's stream, no atomics):
-//   1. the forward fused path in row-state mode: each token's root state (m, s, u);
+//   1. the forward fused path in row-state mode: each token's root state (m, s, u) --
+//      skipped when the caller passes the states its forward call saved;
 //   2. per-token constants (m, log2 s, entropy, upstream gradients, target, row mode);
 //   3. the logits tile is recomputed on MFMA (same tile loop and K order as the forward)
 //      and its gradient dX is written in bf16, row-major [T, Vp] and transposed [V, Tp];
@@ -168,25 +169,55 @@ __global__ __launch_bounds__(kThreads, 1) void dx_tile_kernel(
 }
 
 // Step 4: out[c][r] = in[r][c] for r < R, c < C; out[c][r] = 0 for R <= r < Rp.
+// 64 x 64 tiles through LDS; each lane moves 16 contiguous bytes (8 elements) per global
+// access when the row strides and the tile allow it (the common case), else elements.
 __global__ __launch_bounds__(256) void transpose_pad_kernel(
     const uint16_t* __restrict__ in, int64_t ldin, int64_t R, int64_t C,
     uint16_t* __restrict__ out, int64_t ldout, int64_t Rp) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ uint16_t tile[64][64 + 8];
   const int64_t r0 = (int64_t)blockIdx.x * 64;
   const int64_t c0 = (int64_t)blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  // load: thread -> rows tid / 8 and tid / 8 + 32, columns 8 (tid % 8) .. + 8
+  const bool vec_in = (ldin % 8 == 0) && (c0 + 64 <= C);
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int rr = 4 * k + ty;
-    const int64_t r = r0 + rr, cc = c0 + tx;
-    tile[rr][tx] = (r < R && cc < C) ? in[r * ldin + cc] : (uint16_t)0;
+  for (int h = 0; h < 2; ++h) {
+    const int rr = tid / 8 + 32 * h, cc = 8 * (tid % 8);
+    const int64_t r = r0 + rr;
+    uint16_t v[8];
+    if (r < R && vec_in) {
+      const uint4 q = *reinterpret_cast<const uint4*>(in + r * ldin + c0 + cc);
+      v[0] = q.x & 0xffff; v[1] = q.x >> 16; v[2] = q.y & 0xffff; v[3] = q.y >> 16;
+      v[4] = q.z & 0xffff; v[5] = q.z >> 16; v[6] = q.w & 0xffff; v[7] = q.w >> 16;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = (r < R && c0 + cc + j < C) ? in[r * ldin + c0 + cc + j] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[rr][cc + j] = v[j];
   }
   __syncthreads();
+  // store: thread -> output rows (= input columns) tid / 8 and tid / 8 + 32, 8 consecutive r
+  const bool vec_out = (ldout % 8 == 0) && (r0 + 64 <= Rp);
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int cl = 4 * k + ty;
-    const int64_t cc = c0 + cl, r = r0 + tx;
-    if (cc < C && r < Rp) out[cc * ldout + r] = tile[tx][cl];
+  for (int h = 0; h < 2; ++h) {
+    const int cl = tid / 8 + 32 * h, rl = 8 * (tid % 8);
+    const int64_t cc = c0 + cl;
+    if (cc >= C) continue;
+    uint16_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = tile[rl + j][cl];
+    if (vec_out) {
+      const uint4 q = make_uint4((uint32_t)v[0] | ((uint32_t)v[1] << 16),
+                                 (uint32_t)v[2] | ((uint32_t)v[3] << 16),
+                                 (uint32_t)v[4] | ((uint32_t)v[5] << 16),
+                                 (uint32_t)v[6] | ((uint32_t)v[7] << 16));
+      *reinterpret_cast<uint4*>(out + cc * ldout + r0 + rl) = q;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (r0 + rl + j < Rp) out[cc * ldout + r0 + rl + j] = v[j];
+    }
   }
 }
 
@@ -311,7 +342,7 @@ LinearBackwardWorkspace linear_backward_layout(int64_t T, int64_t V, int64_t d, 
 
 hipError_t launch_linear_backward(const LinearArgs& fwd, const float* g_lp, const float* g_ent,
                                   float* dH, int64_t ld_dh, float* dW, int64_t ld_dw,
-                                  hipStream_t stream) {
+                                  const WireState* states, hipStream_t stream) {
   const int64_t T = fwd.T, V = fwd.V, d = fwd.d;
   const LinearBackwardWorkspace L = linear_backward_layout(T, V, d, fwd.S);
   char* base = static_cast<char*>(fwd.ws);
@@ -319,11 +350,14 @@ hipError_t launch_linear_backward(const LinearArgs& fwd, const float* g_lp, cons
   a.root = reinterpret_cast<WireState*>(base + L.root);
   a.lp = nullptr;
   a.ent = nullptr;
-  hipError_t e = launch_linear_path(a, stream);  // step 1
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (!states) {
+    e = launch_linear_path(a, stream);  // step 1
+    if (e != hipSuccess) return e;
+  }
   GradRowC* rc = reinterpret_cast<GradRowC*>(base + L.rowc);
   hipLaunchKernelGGL(row_consts_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, stream,
-                     a.root, T, V, a.targets, g_lp, g_ent, a.beta, rc);
+                     states ? states : a.root, T, V, a.targets, g_lp, g_ent, a.beta, rc);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   uint16_t* wt = reinterpret_cast<uint16_t*>(base + L.wt);

@@ -159,9 +159,8 @@ __global__ __launch_bounds__(64 * WAVES) void row_reduce_kernel(
   if constexpr (WAVES == 8) {
     const bool has = (t >= 0) && (t < V);
     const float xt = has ? to_f32(X[row * ld + t]) : 0.0f;
-    if (root)
-      root[row] = to_wire(r, xt);
-    else
+    if (root) root[row] = to_wire(r, xt);
+    if (lp_out || ent_out)
       rlk_finalize(r, xt, has, beta, lp_out ? lp_out + row : nullptr,
                    ent_out ? ent_out + row : nullptr);
   } else {
@@ -173,8 +172,8 @@ __global__ __launch_bounds__(64 * WAVES) void row_reduce_kernel(
   }
 }
 
-// Top of the chunk tree across S shard states, then the fp64 finalize (or, when root is
-// given, the row's root state); one thread per row.
+// Top of the chunk tree across S shard states, then the fp64 finalize (when lp or ent is
+// given) and / or the row's root state (when root is given); one thread per row.
 template <int S>
 __global__ __launch_bounds__(256) void shard_merge_kernel(
     const WireState* __restrict__ ws, int64_t T, const int64_t* __restrict__ targets, int64_t V,
@@ -190,9 +189,8 @@ __global__ __launch_bounds__(256) void shard_merge_kernel(
   const bool has = (t >= 0) && (t < V);
   const int64_t owner = has ? (t / shard_cols) : 0;
   const float xt = has ? ws[owner * T + row].xt : 0.0f;
-  if (root)
-    root[row] = to_wire(r, xt);
-  else
+  if (root) root[row] = to_wire(r, xt);
+  if (lp_out || ent_out)
     rlk_finalize(r, xt, has, beta, lp_out ? lp_out + row : nullptr,
                  ent_out ? ent_out + row : nullptr);
 }

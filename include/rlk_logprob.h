@@ -70,6 +70,20 @@ typedef enum {
 #define RLK_OP_LINEAR_BACKWARD 5
 
 /*
+ * A row's reduction state, as the forward calls can save it for the backward calls (the
+ * analogue of saving the log-sum-exp): 24 bytes, 8-byte aligned.  Its contents are the
+ * canonical state the forward reduced to (max logit m, and in fp64 s = sum 2^a,
+ * u = sum 2^a a with a = log2(e) (x - m) / temperature) plus the target's logit; callers
+ * treat it as opaque.  It depends on the logits and the temperature, not on vocab_splits.
+ */
+typedef struct {
+  float m;
+  float target_logit;
+  double s;
+  double u;
+} rlk_row_state;
+
+/*
  * Device workspace, in bytes, that the call `op` needs for these sizes.  Pure host
  * arithmetic (no device access).  `hidden` is ignored unless op == RLK_OP_LINEAR;
  * for RLK_OP_COMPARE only n_tokens is used (vocab, hidden, vocab_splits are ignored).
@@ -88,13 +102,16 @@ rlk_status rlk_workspace_bytes(int op, int64_t n_tokens, int64_t vocab, int64_t 
  *                 and merged (the result bits do not depend on it)
  *   logprob_out   [n_tokens] fp32
  *   entropy_out   [n_tokens] fp32, may be NULL
+ *   row_states_out  [n_tokens] rlk_row_state, may be NULL: the states the backward call
+ *                 can reuse instead of recomputing them
  *   workspace     rlk_workspace_bytes(RLK_OP_FROM_LOGITS, ...) bytes (may be NULL if 0)
  * Sizes: 1 <= vocab < 2^31, 0 <= n_tokens < 2^31.
  */
 rlk_status rlk_logprob_from_logits(const float* logits, int64_t ld_logits, int64_t n_tokens,
                                    int64_t vocab, const int64_t* target_ids, float temperature,
                                    int32_t vocab_splits, float* logprob_out, float* entropy_out,
-                                   void* workspace, size_t workspace_bytes, void* stream);
+                                   rlk_row_state* row_states_out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /*
  * The same two calls on bf16 logits (16-bit patterns, [n_tokens, ld_logits] row-major):
@@ -126,14 +143,14 @@ rlk_status rlk_entropy_bf16(const uint16_t* logits, int64_t ld_logits, int64_t n
  *   hidden_dim    a positive multiple of 64, at most 2^20; ld_hidden, ld_weight >=
  *                 hidden_dim, multiples of 8 and at most 2^22; both base pointers
  *                 16-byte aligned; vocab at most 2^26
- *   other arguments as rlk_logprob_from_logits; entropy_out may be NULL
+ *   other arguments as rlk_logprob_from_logits; entropy_out and row_states_out may be NULL
  */
 rlk_status rlk_linear_logprob(const uint16_t* hidden_bf16, int64_t ld_hidden,
                               const uint16_t* weight_bf16, int64_t ld_weight, int64_t n_tokens,
                               int64_t hidden_dim, int64_t vocab, const int64_t* target_ids,
                               float temperature, int32_t vocab_splits, float* logprob_out,
-                              float* entropy_out, void* workspace, size_t workspace_bytes,
-                              void* stream);
+                              float* entropy_out, rlk_row_state* row_states_out,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Per-token entropy only (no targets).  Bitwise equal to the entropy output of
@@ -155,6 +172,9 @@ rlk_status rlk_entropy(const float* logits, int64_t ld_logits, int64_t n_tokens,
  *                   rlk_logprob_from_logits (target_ids may be NULL if grad_logprob is NULL)
  *   grad_logprob    [n_tokens] fp32 upstream gradient of each row's logprob, or NULL (= 0)
  *   grad_entropy    [n_tokens] fp32 upstream gradient of each row's entropy, or NULL (= 0)
+ *   row_states      [n_tokens] rlk_row_state saved by rlk_logprob_from_logits on the same
+ *                   logits and temperature, or NULL: then they are recomputed (one more read
+ *                   of the logits)
  *   grad_logits     [n_tokens, ld_grad] fp32 output, ld_grad >= vocab; it may be the logits
  *                   array itself (in place) when ld_grad == ld_logits, and must not
  *                   otherwise overlap it
@@ -169,7 +189,8 @@ rlk_status rlk_logprob_backward_from_logits(const float* logits, int64_t ld_logi
                                             int64_t n_tokens, int64_t vocab,
                                             const int64_t* target_ids, float temperature,
                                             int32_t vocab_splits, const float* grad_logprob,
-                                            const float* grad_entropy, float* grad_logits,
+                                            const float* grad_entropy,
+                                            const rlk_row_state* row_states, float* grad_logits,
                                             int64_t ld_grad, void* workspace,
                                             size_t workspace_bytes, void* stream);
 
@@ -187,6 +208,8 @@ rlk_status rlk_logprob_backward_from_logits(const float* logits, int64_t ld_logi
  *   temperature, vocab_splits: as for rlk_linear_logprob (target_ids may be NULL if
  *                   grad_logprob is NULL)
  *   grad_logprob, grad_entropy: [n_tokens] fp32 upstream gradients, or NULL (= 0)
+ *   row_states      [n_tokens] rlk_row_state saved by rlk_linear_logprob on the same
+ *                   inputs and temperature, or NULL: then the forward is recomputed
  *   grad_hidden     [n_tokens, ld_grad_hidden] fp32 output, or NULL (not computed)
  *   grad_weight     [vocab, ld_grad_weight] fp32 output, or NULL (not computed)
  *   workspace       rlk_workspace_bytes(RLK_OP_LINEAR_BACKWARD, ...) bytes, 256-aligned
@@ -199,7 +222,8 @@ rlk_status rlk_linear_logprob_backward(const uint16_t* hidden_bf16, int64_t ld_h
                                        int64_t n_tokens, int64_t hidden_dim, int64_t vocab,
                                        const int64_t* target_ids, float temperature,
                                        int32_t vocab_splits, const float* grad_logprob,
-                                       const float* grad_entropy, float* grad_hidden,
+                                       const float* grad_entropy,
+                                       const rlk_row_state* row_states, float* grad_hidden,
                                        int64_t ld_grad_hidden, float* grad_weight,
                                        int64_t ld_grad_weight, void* workspace,
                                        size_t workspace_bytes, void* stream);

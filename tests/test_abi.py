@@ -69,7 +69,8 @@ def test_workspace_sizes(L):
 
 def call_logits(L, logits=FAKE, ld=1024, T=4, V=1024, targets=FAKE, tau=1.0, S=1, lp=FAKE,
                 ent=FAKE, ws=None, wsb=0):
-    return L.logprob_from_logits_raw(logits, ld, T, V, targets, tau, S, lp, ent, ws, wsb, None)
+    return L.logprob_from_logits_raw(logits, ld, T, V, targets, tau, S, lp, ent, None, ws, wsb,
+                                     None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -176,6 +177,8 @@ def test_backward_workspace(L):
     (dict(wsb=4 * 24 - 1), B.RLK_ERR_WORKSPACE_TOO_SMALL),
     (dict(ws=FAKE + 16), B.RLK_ERR_INVALID_ARGUMENT),
     (dict(T=0, logits=None, grad=None, ws=None, wsb=0), B.RLK_OK),
+    (dict(states=FAKE + 4), B.RLK_ERR_INVALID_ARGUMENT),             # misaligned row states
+    (dict(states=FAKE), B.RLK_ERR_UNSUPPORTED_DEVICE),
     (dict(), B.RLK_ERR_UNSUPPORTED_DEVICE),
 ])
 def test_backward_validation(L, kw, code):
@@ -184,7 +187,7 @@ def test_backward_validation(L, kw, code):
     a.update(kw)
     assert L.lib.rlk_logprob_backward_from_logits(
         a["logits"], a["ld"], a["T"], a["V"], a["targets"], a["tau"], a["S"], a["glp"],
-        a["gent"], a["grad"], a["ldg"], a["ws"], a["wsb"], None) == code
+        a["gent"], a.get("states"), a["grad"], a["ldg"], a["ws"], a["wsb"], None) == code
 
 
 def test_linear_backward_workspace_and_validation(L):
@@ -204,8 +207,8 @@ def test_linear_backward_workspace_and_validation(L):
         a = dict(base)
         a.update(kw)
         return f(a["h"], a["ldh"], a["w"], a["ldw"], a["T"], a["d"], a["V"], a["tg"], a["tau"],
-                 a["S"], a["glp"], a["gent"], a["dh"], a["lddh"], a["dw"], a["lddw"], a["ws"],
-                 a["wsb"], None)
+                 a["S"], a["glp"], a["gent"], a.get("states"), a["dh"], a["lddh"], a["dw"],
+                 a["lddw"], a["ws"], a["wsb"], None)
     assert call(d=96) == B.RLK_ERR_INVALID_ARGUMENT
     assert call(lddh=1000) == B.RLK_ERR_INVALID_ARGUMENT
     assert call(lddw=1000) == B.RLK_ERR_INVALID_ARGUMENT
@@ -217,11 +220,12 @@ def test_linear_backward_workspace_and_validation(L):
     assert call(T=0, h=None, w=None, ws=None, wsb=0) == B.RLK_OK
     assert call() == B.RLK_ERR_UNSUPPORTED_DEVICE
     assert call(tg=None, glp=None, gent=FAKE) == B.RLK_ERR_UNSUPPORTED_DEVICE
+    assert call(states=FAKE + 4) == B.RLK_ERR_INVALID_ARGUMENT
 
 
 def call_linear(L, h=FAKE, ldh=2048, w=FAKE, ldw=2048, T=4, d=2048, V=1000, tg=FAKE, tau=1.0,
                 S=1, lp=FAKE, ent=None, ws=FAKE, wsb=1 << 30):
-    return L.linear_logprob_raw(h, ldh, w, ldw, T, d, V, tg, tau, S, lp, ent, ws, wsb, None)
+    return L.linear_logprob_raw(h, ldh, w, ldw, T, d, V, tg, tau, S, lp, ent, None, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -186,3 +186,23 @@ def test_qwen3_vocab_split_batch_order_repeats_bitwise(lib, cfg2):
         assert torch.equal(gs.view(torch.int32), ref[lo:hi].view(torch.int32))
     again = lib.logprob_backward_from_logits(xd, td, 1.0, 1, gld, ged).cpu()
     assert torch.equal(again.view(torch.int32), ref.view(torch.int32))
+
+
+def test_saved_row_states_give_the_same_bits(lib):
+    """Row states saved by the forward call (at any vocab split) skip the recompute and give
+    the recomputing backward's bits; the forward outputs do not change when they are saved."""
+    import torch
+    T, V = 40, 30011
+    case = S.random_logits_case(T, V, 3.0, seed=86)
+    gl, ge = weights(T, 87)
+    xd, td, gld, ged = dev(case.x), dev(case.targets), dev(gl), dev(ge)
+    announce("grad with saved row states")
+    ref = lib.logprob_backward_from_logits(xd, td, 0.7, 1, gld, ged).cpu()
+    lp0, ent0 = lib.logprob_from_logits(xd, td, 0.7, 1)
+    for split in (1, 4):
+        states = lib.row_states_buffer(T)
+        lp, ent = lib.logprob_from_logits(xd, td, 0.7, split, row_states=states)
+        assert torch.equal(lp.view(torch.int32), lp0.view(torch.int32))
+        assert torch.equal(ent.view(torch.int32), ent0.view(torch.int32))
+        g = lib.logprob_backward_from_logits(xd, td, 0.7, 1, gld, ged, row_states=states).cpu()
+        assert torch.equal(g.view(torch.int32), ref.view(torch.int32)), split

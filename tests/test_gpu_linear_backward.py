@@ -145,3 +145,23 @@ def test_qwen3_vocab_full_hidden_vs_oracle(lib):
     announce("linear backward T=256 repeat and split 8")
     dh2, dw2 = run_bwd(lib, hd, wd, td, 1.0, 8, gld, ged)
     assert bitwise_equal(dh2, dh) and bitwise_equal(dw2, dw)
+
+
+def test_saved_row_states_give_the_same_bits(lib):
+    import torch
+    T, d, V = 200, 128, 9001
+    case = S.random_fused_case(T, d, V, seed=104, w_sigma=3.0 / math.sqrt(d), temperature=0.7)
+    gl, ge = weights(T, 105)
+    hd, wd, td = bits_dev(case.h_bits), bits_dev(case.w_bits), dev(case.targets)
+    gld, ged = dev(gl), dev(ge)
+    announce("linear backward with saved row states")
+    dh0, dw0 = lib.linear_logprob_backward(hd, wd, td, 0.7, 1, gld, ged)
+    lp0, ent0 = lib.linear_logprob(hd, wd, td, 0.7, 1)
+    for split in (1, 2):
+        states = lib.row_states_buffer(T)
+        lp, ent = lib.linear_logprob(hd, wd, td, 0.7, split, row_states=states)
+        assert torch.equal(lp.view(torch.int32), lp0.view(torch.int32))
+        assert torch.equal(ent.view(torch.int32), ent0.view(torch.int32))
+        dh, dw = lib.linear_logprob_backward(hd, wd, td, 0.7, 1, gld, ged, row_states=states)
+        assert torch.equal(dh.view(torch.int32), dh0.view(torch.int32)), split
+        assert torch.equal(dw.view(torch.int32), dw0.view(torch.int32)), split
