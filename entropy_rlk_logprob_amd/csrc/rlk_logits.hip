@@ -6,9 +6,11 @@
 //   * within a chunk, quad q covers chunk columns [4q, 4q+4) and belongs to lane q % 64;
 //     a lane's quads k = 0, 1, 2, ... (q = lane + 64 k) are grouped four at a time into
 //     16-element leaves;
-//   * leaf: m = max of its 16 values, then fp32 2^{c (x - m)} terms summed pairwise
-//     (within each quad, then quad pairs); leaves are folded into the lane's fp64 state
-//     in increasing k with rlk_merge;
+//   * groups are folded into the lane's state in increasing k (fold_group): the state
+//     keeps the running max m and fp64 sums relative to it; a group whose max exceeds m
+//     first rebases the sums to that max, then its fp32 terms 2^{c (x - m)} and
+//     2^{c (x - m)} c (x - m) are summed pairwise (within each quad, then quad pairs)
+//     and added in;
 //   * lanes: xor-butterfly (32, 16, 8, 4, 2, 1); chunks: ((0,1),(2,3)),((4,5),(6,7)).
 // A vocab shard (split count S) owns 8/S consecutive chunks, reduces them in one
 // workgroup exactly as the unsplit case does, and hands its state to the merge kernel,
@@ -101,9 +103,103 @@ __device__ __forceinline__ void load_group_masked(const E* __restrict__ p, int l
   }
 }
 
+// Wide-load form of a chunk's last (partial) group: a quad wholly inside the chunk takes
+// the wide load, the others element loads with -inf beyond column n (the identity's
+// contribution; bf16 -inf is 0xff80).  It yields the values load_group_masked yields, so
+// the leaf sees the same bits either way.
+template <typename E>
+__device__ __forceinline__ void load_raw_masked(const E* __restrict__ p, int lane, int g, int n,
+                                                RawGroup<E>& r) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = lane + 64 * (4 * g + i);
+    if (4 * q + 4 <= n) {
+      if constexpr (sizeof(E) == 4)
+        r.q[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + q);
+      else
+        r.q[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p) + q);
+    } else if constexpr (sizeof(E) == 4) {
+      f32x4 v;
+      v.x = (4 * q + 0 < n) ? __builtin_nontemporal_load(p + 4 * q + 0) : kNegInf;
+      v.y = (4 * q + 1 < n) ? __builtin_nontemporal_load(p + 4 * q + 1) : kNegInf;
+      v.z = (4 * q + 2 < n) ? __builtin_nontemporal_load(p + 4 * q + 2) : kNegInf;
+      v.w = (4 * q + 3 < n) ? __builtin_nontemporal_load(p + 4 * q + 3) : kNegInf;
+      r.q[i] = v;
+    } else {
+      uint32_t e[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        e[j] = (4 * q + j < n) ? (uint32_t)__builtin_nontemporal_load(p + 4 * q + j) : 0xff80u;
+      r.q[i] = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+    }
+  }
+}
+
+// A lane's running state over its groups: (m, s, u) of everything folded so far with
+// s and u relative to the running max m, and ref = m, or 0 while m = -inf (every value
+// seen so far is -inf and contributes 0).  A group whose max exceeds m first rebases the
+// sums to the new max, in fp64: s <- s 2^d, u <- (u + d s) 2^d with d = c (m_old - m_new);
+// its 16 terms 2^a and 2^a a, a = c (x - ref) <= 0, are then summed pairwise in fp32
+// (within each quad, then quad pairs) and added to s and u.
+struct LaneFold {
+  State st;
+  float ref;
+};
+
+__device__ __forceinline__ LaneFold lane_fold_init() { return LaneFold{identity_state(), 0.0f}; }
+
+__device__ __forceinline__ void fold_group(LaneFold& f, const float* v, float c) {
+  float gm = v[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) gm = fmaxf(gm, v[i]);
+  if (gm > f.st.m) {
+    const float d = (f.st.m - gm) * c;  // < 0; -inf when m = -inf or gm = +inf
+    const double scale = (double)exp2_hw(d);
+    const double dc = (double)fmaxf(d, -kMaxFloat);  // keeps 0 * (-inf) out of u
+    f.st.u = (f.st.u + dc * f.st.s) * scale;
+    f.st.s = f.st.s * scale;
+    f.st.m = gm;
+    f.ref = gm;
+  }
+  float e[16], t[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float a = (v[i] - f.ref) * c;
+    e[i] = exp2_hw(a);
+    t[i] = mul_zero_wins(e[i], a);  // 0 where e = 0 (a = -inf)
+  }
+  float sq[4], uq[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sq[j] = (e[4 * j] + e[4 * j + 1]) + (e[4 * j + 2] + e[4 * j + 3]);
+    uq[j] = (t[4 * j] + t[4 * j + 1]) + (t[4 * j + 2] + t[4 * j + 3]);
+  }
+  f.st.s += (double)((sq[0] + sq[1]) + (sq[2] + sq[3]));
+  f.st.u += (double)((uq[0] + uq[1]) + (uq[2] + uq[3]));
+}
+
+template <typename E>
+__device__ __forceinline__ void issue_group(const E* __restrict__ p, int lane, int g, int n,
+                                            int n_full, RawGroup<E>& r) {
+  if (g < n_full)
+    load_raw(p, lane, g, r);
+  else
+    load_raw_masked(p, lane, g, n, r);
+}
+
+template <typename E>
+__device__ __forceinline__ void fold_raw(LaneFold& f, const RawGroup<E>& r, float c) {
+  Quad4 v;
+  widen(r, v);
+  fold_group(f, v.v, c);
+}
+
 // One workgroup = one (row, shard); WAVES = 8 / S chunks per shard, one wave per chunk.
+// Eight waves per SIMD (at most 64 VGPRs) keep a row's whole workgroup and three more
+// resident per CU, so a 1024-row launch runs as a single round.
 template <typename E, int WAVES, bool VEC>
-__global__ __launch_bounds__(64 * WAVES) void row_reduce_kernel(
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void row_reduce_kernel(
     const E* __restrict__ X, int64_t ld, int64_t T, int64_t V, int64_t Vc,
     const int64_t* __restrict__ targets, float c, double beta, float* __restrict__ lp_out,
     float* __restrict__ ent_out, WireState* __restrict__ ws, WireState* __restrict__ root) {
@@ -117,36 +213,35 @@ __global__ __launch_bounds__(64 * WAVES) void row_reduce_kernel(
   const int n = (int)(hi - lo);
   const E* __restrict__ p = X + row * ld + lo;
 
-  State st = identity_state();
+  LaneFold f = lane_fold_init();
   const int n_groups = (((n + 3) >> 2) + 255) >> 8;  // ceil(ceil(n/4) / 256)
   const int n_full = (n >> 2) >> 8;                   // groups with every column inside
   if constexpr (VEC) {
-    // Double buffer: the loads of group g + 1 are in flight while group g is reduced.
+    // Double buffer: the loads of the next group are in flight while a group is folded,
+    // the chunk's partial last group included, so no load latency is exposed at the
+    // chunk's end.
     // (Deeper prefetch measured no faster: at 8 waves per SIMD the bf16 kernel is bound by
     // VALU issue, the fp32 kernel by HBM.)
-    if (n_full > 0) {
-      RawGroup<E> cur, nxt;
-      load_raw(p, lane, 0, cur);
-      for (int g = 0; g < n_full; ++g) {
-        if (g + 1 < n_full) load_raw(p, lane, g + 1, nxt);
-        Quad4 v;
-        widen(cur, v);
-        st = rlk_merge(st, leaf16(v.v, c), c);
-        cur = nxt;
-      }
+    RawGroup<E> cur, nxt;
+    if (n_groups > 0) issue_group(p, lane, 0, n, n_full, cur);
+    for (int g = 0; g < n_groups; ++g) {
+      if (g + 1 < n_groups) issue_group(p, lane, g + 1, n, n_full, nxt);
+      fold_raw(f, cur, c);
+      cur = nxt;
     }
   } else {
     for (int g = 0; g < n_full; ++g) {
       Quad4 v;
       load_group_scalar(p, lane, g, v);
-      st = rlk_merge(st, leaf16(v.v, c), c);
+      fold_group(f, v.v, c);
+    }
+    for (int g = n_full; g < n_groups; ++g) {
+      Quad4 q;
+      load_group_masked(p, lane, g, n, q);
+      fold_group(f, q.v, c);
     }
   }
-  for (int g = n_full; g < n_groups; ++g) {
-    Quad4 q;
-    load_group_masked(p, lane, g, n, q);
-    st = rlk_merge(st, leaf16(q.v, c), c);
-  }
+  State st = f.st;
   st = wave_tree(st, c);
 
   __shared__ State chunk_state[WAVES];
