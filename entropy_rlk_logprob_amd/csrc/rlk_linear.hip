@@ -9,10 +9,10 @@
 //     64-wide K steps in increasing order, each four v_mfma_f32_32x32x16_bf16 steps
 //     (16 consecutive k each);
 //   * tile state of (token, tile): the 256 vocab rows split into two 128-row halves, each
-//     into four 32-row MFMA blocks; within a block a lane holds 16 rows
-//     8*(i/4) + 4*(lane/32) + (i%4), i = 0..15, which form one 16-element leaf (the same
-//     leaf as on the logits path: pairwise fp32 sums); the four leaves of a lane merge as
-//     ((0,1),(2,3)), then lane halves (lane < 32 first), then the two 128-row halves;
+//     into four 32-row MFMA blocks; within block a a lane holds 16 rows
+//     8*(i/4) + 4*(lane/32) + (i%4), i = 0..15; a lane's 64 rows of a half form one leaf
+//     (leaf64: their max, then pairwise fp32 sums within quads, quad pairs and blocks
+//     ((0,1),(2,3))), then lane halves merge (lane < 32 first), then the two 128-row halves;
 //   * tiles of a chunk: balanced binary tree over tile index (padded with identities);
 //     chunks: ((0,1),(2,3)),((4,5),(6,7)), the top log2(S) levels in the shard merge.
 //
@@ -54,6 +54,43 @@ struct TileGeom {
   int64_t block_tiles;  // tiles per block of the tile tree: max(1, P / 8), P = next_pow2(tpc)
   int64_t Vc, V, T;
 };
+
+// State of the 64 vocabulary rows a lane holds for one token (four 16-row groups, one per
+// MFMA block): m = their max, then fp32 terms 2^{c (x - m)} and 2^{c (x - m)} c (x - m)
+// summed pairwise -- within each quad, quad pairs, then the groups as ((0,1),(2,3)).
+// With every value in registers the max comes first and no state merge is needed.
+__device__ __forceinline__ State leaf64(const float (&v)[4][16], float c) {
+  float mg = v[0][0];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int i = (a == 0 ? 1 : 0); i < 16; ++i) mg = fmaxf(mg, v[a][i]);
+  const float mref = (mg == kNegInf) ? 0.0f : mg;
+  float sg[4], ug[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    float e[16], t[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float x = (v[a][i] - mref) * c;
+      e[i] = exp2_hw(x);
+      t[i] = mul_zero_wins(e[i], x);  // 0 where e = 0 (a masked row)
+    }
+    float sq[4], uq[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sq[j] = (e[4 * j] + e[4 * j + 1]) + (e[4 * j + 2] + e[4 * j + 3]);
+      uq[j] = (t[4 * j] + t[4 * j + 1]) + (t[4 * j + 2] + t[4 * j + 3]);
+    }
+    sg[a] = (sq[0] + sq[1]) + (sq[2] + sq[3]);
+    ug[a] = (uq[0] + uq[1]) + (uq[2] + uq[3]);
+  }
+  State r;
+  r.m = mg;
+  r.s = (double)((sg[0] + sg[1]) + (sg[2] + sg[3]));
+  r.u = (double)((ug[0] + ug[1]) + (ug[2] + ug[3]));
+  return r;
+}
 
 __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
     const uint16_t* __restrict__ H, int64_t ldh, const uint16_t* __restrict__ W, int64_t ldw,
@@ -138,21 +175,18 @@ __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
         target_logit[tok] = xt;
       }
 
-      State leaf[4];
+      float v[4][16];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        float v[16];
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          v[i] = acc[a][b][i];
+          v[a][i] = acc[a][b][i];
           if constexpr (decltype(masked)::value) {
             const int vr = wv * 128 + a * 32 + 8 * (i >> 2) + 4 * fhalf + (i & 3);
-            v[i] = (vr < n_valid) ? v[i] : kNegInf;
+            v[a][i] = (vr < n_valid) ? v[a][i] : kNegInf;
           }
         }
-        leaf[a] = leaf16(v, c);
-      }
-      State st = rlk_merge(rlk_merge(leaf[0], leaf[1], c), rlk_merge(leaf[2], leaf[3], c), c);
+      const State st = leaf64(v, c);
       const State o = shfl_xor_state(st, 32);
       half_state[b] = fhalf ? rlk_merge(o, st, c) : rlk_merge(st, o, c);
     }

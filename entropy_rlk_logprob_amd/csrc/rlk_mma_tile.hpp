@@ -117,7 +117,10 @@ __device__ __forceinline__ void mma_tile(const uint16_t* __restrict__ At, int64_
   issue_stage(0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     // Stage kt has landed for every wave, and every wave is done reading stage kt - 1,
-    // whose buffer the loads of stage kt + 1 now overwrite.
+    // whose buffer the loads of stage kt + 1 now overwrite.  A wave waits at normal issue
+    // priority and runs its MFMA steps at raised priority, so that the SIMD's arbiter
+    // favours the wave that is feeding the matrix unit.
+    __builtin_amdgcn_s_setprio(0);
     wait_dma();
     lds_barrier();
     const char* wb = smem + (kt & 1) * kStageBytes;
@@ -136,6 +139,7 @@ __device__ __forceinline__ void mma_tile(const uint16_t* __restrict__ At, int64_
             bf16x8, *reinterpret_cast<const U4*>(hb + lds_offset(wt * 64 + b * 32 + frow, c16)));
     };
     read_frags(0, 0);
+    __builtin_amdgcn_s_setprio(1);
     sched_group(kSchedDsRead, 6);
     // Loads of stage kt + 1 into the other buffer.  Issued on every stage (the last one
     // repeats stage nk - 1 into the idle buffer) so that they stay in this scheduling
@@ -174,6 +178,7 @@ __device__ __forceinline__ void mma_tile(const uint16_t* __restrict__ At, int64_
       }
     }
   }
+  __builtin_amdgcn_s_setprio(0);
   wait_dma();  // the repeated last-stage loads land before the caller reuses the LDS
 }
 
