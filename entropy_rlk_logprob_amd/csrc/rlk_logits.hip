@@ -7,10 +7,10 @@
 //     a lane's quads k = 0, 1, 2, ... (q = lane + 64 k) are grouped four at a time into
 //     16-element leaves;
 //   * groups are folded into the lane's state in increasing k (fold_group): the state
-//     keeps the running max m and fp64 sums relative to it; a group whose max exceeds m
-//     first rebases the sums to that max, then its fp32 terms 2^{c (x - m)} and
-//     2^{c (x - m)} c (x - m) are summed pairwise (within each quad, then quad pairs)
-//     and added in;
+//     keeps a reference m (the lane's running max, up to one unit of c (x - m)) and fp64
+//     sums relative to it; a group whose max exceeds m by more than that first rebases
+//     the sums to its max, then its fp32 terms 2^{c (x - m)} and 2^{c (x - m)} c (x - m)
+//     are summed pairwise (within each quad, then quad pairs) and added in;
 //   * lanes: xor-butterfly (32, 16, 8, 4, 2, 1); chunks: ((0,1),(2,3)),((4,5),(6,7)).
 // A vocab shard (split count S) owns 8/S consecutive chunks, reduces them in one
 // workgroup exactly as the unsplit case does, and hands its state to the merge kernel,
@@ -136,11 +136,14 @@ __device__ __forceinline__ void load_raw_masked(const E* __restrict__ p, int lan
 }
 
 // A lane's running state over its groups: (m, s, u) of everything folded so far with
-// s and u relative to the running max m, and ref = m, or 0 while m = -inf (every value
-// seen so far is -inf and contributes 0).  A group whose max exceeds m first rebases the
-// sums to the new max, in fp64: s <- s 2^d, u <- (u + d s) 2^d with d = c (m_old - m_new);
-// its 16 terms 2^a and 2^a a, a = c (x - ref) <= 0, are then summed pairwise in fp32
-// (within each quad, then quad pairs) and added to s and u.
+// s and u relative to the reference m, and ref = m, or 0 while m = -inf (every value
+// seen so far is -inf and contributes 0).  A group whose max g exceeds the reference by
+// more than one unit of a, c (g - m) > 1, first rebases the sums to g in fp64:
+// s <- s 2^d, u <- (u + d s) 2^d with d = c (m - g); its 16 terms 2^a and 2^a a,
+// a = c (x - ref) <= 1, are then summed pairwise in fp32 (within each quad, then quad
+// pairs) and added to s and u.  So m stays within ln(2) tau of the lane's max, every
+// rebase at least halves the weight of what came before (a long run of tiny rebases would
+// otherwise compound the rounding of their factors), and the sums stay far from overflow.
 struct LaneFold {
   State st;
   float ref;
@@ -152,8 +155,8 @@ __device__ __forceinline__ void fold_group(LaneFold& f, const float* v, float c)
   float gm = v[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) gm = fmaxf(gm, v[i]);
-  if (gm > f.st.m) {
-    const float d = (f.st.m - gm) * c;  // < 0; -inf when m = -inf or gm = +inf
+  if ((gm - f.st.m) * c > 1.0f) {      // false for NaN: a NaN group poisons s below
+    const float d = (f.st.m - gm) * c;  // < -1; -inf when m = -inf or gm = +inf
     const double scale = (double)exp2_hw(d);
     const double dc = (double)fmaxf(d, -kMaxFloat);  // keeps 0 * (-inf) out of u
     f.st.u = (f.st.u + dc * f.st.s) * scale;

@@ -198,6 +198,32 @@ def test_nonfinite_rows_and_targets(lib):
     assert abs(lps[0] - lpm[0]) <= TOL_LOGITS and abs(ents[0] - entm[0]) <= TOL_LOGITS
 
 
+@pytest.mark.parametrize("tau", [1.0, 0.7])
+def test_monotone_and_sawtooth_rows_vs_oracle(lib, tau):
+    """Rows whose running max rises at (almost) every group of every lane, which makes each
+    lane rebase its sums again and again, next to falling, sawtooth and offset rows."""
+    V = 151936
+    i = np.arange(V, dtype=np.float64)
+    rows = [1e-6 * i, 1e-5 * i, 3e-6 * i - 0.2, 1e-3 * i, -1e-5 * i, (i % 1024) * 1e-3,
+            1000.0 + 1e-5 * i, -50.0 + 2e-4 * i]
+    x = np.stack(rows).astype(np.float32)
+    T = x.shape[0]
+    t = np.array([V - 1, 0, V // 2, V - 2, 0, 1023, 77, V - 1])
+    announce(f"logits monotone and sawtooth rows V={V} tau={tau}")
+    olp, oent = oracle.logprob_entropy(x, t, tau)
+    ref = None
+    for split in (1, 8):
+        lp, ent = run_logits(lib, x, t, tau, split)
+        assert max_abs(lp, olp) <= TOL_LOGITS, (split, np.abs(lp - olp).max())
+        assert max_abs(ent, oent) <= TOL_LOGITS, (split, np.abs(ent - oent).max())
+        if ref is None:
+            ref = (lp, ent)
+        else:
+            assert bitwise_equal(lp, ref[0]) and bitwise_equal(ent, ref[1])
+    print(f"max_abs_vs_fp64 logprob={max_abs(lp, olp):.3e} entropy={max_abs(ent, oent):.3e}")
+    assert T == len(t)
+
+
 def test_empty_batch(lib):
     import torch
     announce("logits T=0")
