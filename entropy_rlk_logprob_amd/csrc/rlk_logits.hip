@@ -16,8 +16,9 @@
 // workgroup exactly as the unsplit case does, and hands its state to the merge kernel,
 // which applies the top S-leaf part of the same chunk tree.
 //
-// Layout and launch: one workgroup per (row, shard), one wave per chunk; each lane
-// streams 16-byte loads whose 64 lanes cover 1 KiB of contiguous HBM per instruction.
+// Layout and launch: one workgroup per (row, shard), one wave per chunk (bf16: per two
+// chunks of the shard); each lane streams 16-byte loads (bf16: 8-byte) whose 64 lanes
+// cover 1 KiB (512 bytes) of contiguous HBM per instruction.
 // The loads carry the non-temporal hint: every logit is read exactly once.
 
 #include "rlk_launch.hpp"
@@ -197,64 +198,142 @@ __device__ __forceinline__ void fold_raw(LaneFold& f, const RawGroup<E>& r, floa
   fold_group(f, v.v, c);
 }
 
-// One workgroup = one (row, shard); WAVES = 8 / S chunks per shard, one wave per chunk.
-// Eight waves per SIMD (at most 64 VGPRs) keep a row's whole workgroup and three more
-// resident per CU, so a 1024-row launch runs as a single round.
-template <typename E, int WAVES, bool VEC>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(8, 8)))
+// Chunks per wave for a shard of CPS chunks.  fp32 logits: one (8192 waves for 1024 rows,
+// all resident at eight waves per SIMD, the most bytes in flight for an HBM-bound stream).
+// bf16 logits, which are bound by VALU issue: two when the shard has two or more (4096
+// waves, one round at four or more per SIMD), which leaves the registers to unroll the
+// double buffer so that no register copies are issued per group -- 6% faster.
+template <typename E>
+constexpr int chunks_per_wave(int cps) { return (sizeof(E) == 2 && cps >= 2) ? 2 : 1; }
+template <typename E>
+constexpr int waves_for(int cps) { return cps / chunks_per_wave<E>(cps); }
+
+// Chunk k (0 <= k < n of the chunk) of one wave's stream of groups over its chunks.
+template <typename E>
+struct ChunkRef {
+  const E* p;  // first column of the chunk in this row
+  int n;       // columns
+  int n_groups, n_full;
+};
+
+template <typename E>
+__device__ __forceinline__ ChunkRef<E> chunk_ref(const E* row_base, int64_t chunk, int64_t Vc,
+                                                 int64_t V) {
+  const int64_t lo = min(chunk * Vc, V);
+  const int64_t hi = min(lo + Vc, V);
+  ChunkRef<E> r;
+  r.p = row_base + lo;
+  r.n = (int)(hi - lo);
+  r.n_groups = (((r.n + 3) >> 2) + 255) >> 8;  // ceil(ceil(n/4) / 256)
+  r.n_full = (r.n >> 2) >> 8;                   // groups with every column inside
+  return r;
+}
+
+// One workgroup = one (row, shard) of CPS = 8 / S chunks; wave w folds chunks w and
+// w + WAVES of the shard (or just w when CPS = 1), each into its own lane state.  Which
+// wave folds a chunk does not change its bits.
+template <typename E, int CPS, bool VEC>
+__global__ __launch_bounds__(64 * waves_for<E>(CPS))
+__attribute__((amdgpu_waves_per_eu(chunks_per_wave<E>(CPS) == 2 ? 4 : 8)))
 void row_reduce_kernel(
     const E* __restrict__ X, int64_t ld, int64_t T, int64_t V, int64_t Vc,
     const int64_t* __restrict__ targets, float c, double beta, float* __restrict__ lp_out,
     float* __restrict__ ent_out, WireState* __restrict__ ws, WireState* __restrict__ root) {
+  constexpr int WAVES = waves_for<E>(CPS);
+  constexpr int CPW = chunks_per_wave<E>(CPS);
   const int64_t row = blockIdx.x;
   const int shard = blockIdx.y;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int64_t chunk = (int64_t)shard * WAVES + wave;
-  const int64_t lo = min(chunk * Vc, V);
-  const int64_t hi = min(lo + Vc, V);
-  const int n = (int)(hi - lo);
-  const E* __restrict__ p = X + row * ld + lo;
+  const E* __restrict__ base = X + row * ld;
+  const ChunkRef<E> A = chunk_ref(base, (int64_t)shard * CPS + wave, Vc, V);
+  ChunkRef<E> B = A;
+  B.n_groups = 0;
+  if constexpr (CPW == 2) B = chunk_ref(base, (int64_t)shard * CPS + wave + WAVES, Vc, V);
 
-  LaneFold f = lane_fold_init();
-  const int n_groups = (((n + 3) >> 2) + 255) >> 8;  // ceil(ceil(n/4) / 256)
-  const int n_full = (n >> 2) >> 8;                   // groups with every column inside
+  // A's lane state, then B's: one LaneFold, saved to sa and reset at the chunk boundary
+  // (a uniform branch), so that the fold never selects its state by a runtime index.
+  State sa = identity_state(), sb = identity_state();
   if constexpr (VEC) {
-    // Double buffer: the loads of the next group are in flight while a group is folded,
-    // the chunk's partial last group included, so no load latency is exposed at the
-    // chunk's end.
-    // (Deeper prefetch measured no faster: at 8 waves per SIMD the bf16 kernel is bound by
-    // VALU issue, the fp32 kernel by HBM.)
-    RawGroup<E> cur, nxt;
-    if (n_groups > 0) issue_group(p, lane, 0, n, n_full, cur);
-    for (int g = 0; g < n_groups; ++g) {
-      if (g + 1 < n_groups) issue_group(p, lane, g + 1, n, n_full, nxt);
-      fold_raw(f, cur, c);
-      cur = nxt;
+    // One stream of groups over the wave's chunks (A's, then B's), double buffered: the
+    // loads of the next group are in flight while a group is folded, across the chunk
+    // boundary and into each chunk's partial last group, so no load latency is exposed
+    // before the end of the stream.  (Deeper prefetch measured no faster.)
+    const int n = A.n_groups + B.n_groups;
+    auto issue = [&](int j, RawGroup<E>& r) {
+      if (j < A.n_groups)
+        issue_group(A.p, lane, j, A.n, A.n_full, r);
+      else
+        issue_group(B.p, lane, j - A.n_groups, B.n, B.n_full, r);
+    };
+    LaneFold f = lane_fold_init();
+    auto fold = [&](int j, const RawGroup<E>& r) {
+      if (j == A.n_groups) {
+        sa = f.st;
+        f = lane_fold_init();
+      }
+      fold_raw(f, r, c);
+    };
+    if constexpr (CPW == 2) {
+      // Unrolled by two: the buffers swap roles without copies.
+      RawGroup<E> b0, b1;
+      if (n > 0) issue(0, b0);
+      if (n > 1) issue(1, b1);
+      for (int j = 0; j < n; j += 2) {
+        fold(j, b0);
+        if (j + 2 < n) issue(j + 2, b0);
+        if (j + 1 >= n) break;
+        fold(j + 1, b1);
+        if (j + 3 < n) issue(j + 3, b1);
+      }
+    } else {
+      RawGroup<E> cur, nxt;
+      if (n > 0) issue(0, cur);
+      for (int j = 0; j < n; ++j) {
+        if (j + 1 < n) issue(j + 1, nxt);
+        fold(j, cur);
+        cur = nxt;
+      }
     }
+    if (n > A.n_groups)
+      sb = f.st;
+    else
+      sa = f.st;
   } else {
-    for (int g = 0; g < n_full; ++g) {
-      Quad4 v;
-      load_group_scalar(p, lane, g, v);
-      fold_group(f, v.v, c);
-    }
-    for (int g = n_full; g < n_groups; ++g) {
-      Quad4 q;
-      load_group_masked(p, lane, g, n, q);
-      fold_group(f, q.v, c);
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const ChunkRef<E>& C = i == 0 ? A : B;
+      LaneFold f = lane_fold_init();
+      for (int g = 0; g < C.n_full; ++g) {
+        Quad4 v;
+        load_group_scalar(C.p, lane, g, v);
+        fold_group(f, v.v, c);
+      }
+      for (int g = C.n_full; g < C.n_groups; ++g) {
+        Quad4 q;
+        load_group_masked(C.p, lane, g, C.n, q);
+        fold_group(f, q.v, c);
+      }
+      if (i == 0)
+        sa = f.st;
+      else
+        sb = f.st;
     }
   }
-  State st = f.st;
-  st = wave_tree(st, c);
 
-  __shared__ State chunk_state[WAVES];
-  if (lane == 0) chunk_state[wave] = st;
+  __shared__ State chunk_state[CPS];
+  sa = wave_tree(sa, c);
+  if (lane == 0) chunk_state[wave] = sa;
+  if constexpr (CPW == 2) {
+    sb = wave_tree(sb, c);
+    if (lane == 0) chunk_state[wave + WAVES] = sb;
+  }
   __syncthreads();
   if (threadIdx.x != 0) return;
 
-  const State r = tree8(chunk_state, WAVES, c);
+  const State r = tree8(chunk_state, CPS, c);
   const int64_t t = targets ? targets[row] : -1;
-  if constexpr (WAVES == 8) {
+  if constexpr (CPS == 8) {
     const bool has = (t >= 0) && (t < V);
     const float xt = has ? to_f32(X[row * ld + t]) : 0.0f;
     if (root) root[row] = to_wire(r, xt);
@@ -262,8 +341,8 @@ void row_reduce_kernel(
       rlk_finalize(r, xt, has, beta, lp_out ? lp_out + row : nullptr,
                    ent_out ? ent_out + row : nullptr);
   } else {
-    const int64_t s_lo = min((int64_t)shard * WAVES * Vc, V);
-    const int64_t s_hi = min(s_lo + (int64_t)WAVES * Vc, V);
+    const int64_t s_lo = min((int64_t)shard * CPS * Vc, V);
+    const int64_t s_hi = min(s_lo + (int64_t)CPS * Vc, V);
     const bool mine = (t >= s_lo) && (t < s_hi);
     const float xt = mine ? to_f32(X[row * ld + t]) : 0.0f;
     ws[(int64_t)shard * T + row] = to_wire(r, xt);
@@ -293,23 +372,23 @@ __global__ __launch_bounds__(256) void shard_merge_kernel(
                  ent_out ? ent_out + row : nullptr);
 }
 
-template <typename E, int WAVES>
+template <typename E, int CPS>
 hipError_t launch_rows_t(const E* X, const LogitsArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.T, (unsigned)(8 / WAVES));
-  const dim3 block(64 * WAVES);
+  const dim3 grid((unsigned)a.T, (unsigned)(8 / CPS));
+  const dim3 block(64 * waves_for<E>(CPS));
   if (a.vec)
-    hipLaunchKernelGGL((row_reduce_kernel<E, WAVES, true>), grid, block, 0, stream, X, a.ld, a.T,
+    hipLaunchKernelGGL((row_reduce_kernel<E, CPS, true>), grid, block, 0, stream, X, a.ld, a.T,
                        a.V, a.Vc, a.targets, a.c, a.beta, a.lp, a.ent, a.ws, a.root);
   else
-    hipLaunchKernelGGL((row_reduce_kernel<E, WAVES, false>), grid, block, 0, stream, X, a.ld, a.T,
+    hipLaunchKernelGGL((row_reduce_kernel<E, CPS, false>), grid, block, 0, stream, X, a.ld, a.T,
                        a.V, a.Vc, a.targets, a.c, a.beta, a.lp, a.ent, a.ws, a.root);
   return hipGetLastError();
 }
 
-template <int WAVES>
+template <int CPS>
 hipError_t launch_rows(const LogitsArgs& a, hipStream_t stream) {
-  return a.Xh ? launch_rows_t<uint16_t, WAVES>(a.Xh, a, stream)
-              : launch_rows_t<float, WAVES>(a.X, a, stream);
+  return a.Xh ? launch_rows_t<uint16_t, CPS>(a.Xh, a, stream)
+              : launch_rows_t<float, CPS>(a.X, a, stream);
 }
 
 }  // namespace
