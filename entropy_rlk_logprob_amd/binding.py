@@ -37,6 +37,18 @@ class RlkError(RuntimeError):
         self.status = status
 
 
+def _require(cond: bool, msg: str):
+    """Argument check that survives `python -O` (unlike assert)."""
+    if not cond:
+        raise ValueError(msg)
+
+
+def _same_device(device, *tensors):
+    for t in tensors:
+        if t is not None:
+            _require(t.device == device, f"tensor on {t.device}, expected {device}")
+
+
 _c_i64 = ctypes.c_int64
 _c_p = ctypes.c_void_p
 
@@ -132,10 +144,17 @@ class Library:
 
     # ------------------------------------------------------------------ torch wrappers
     @staticmethod
-    def _stream_handle(stream) -> int:
+    def _stream_handle(stream, device) -> int:
         import torch
-        s = stream if stream is not None else torch.cuda.current_stream()
+        s = stream if stream is not None else torch.cuda.current_stream(device)
         return int(s.cuda_stream)
+
+    @staticmethod
+    def _on(device):
+        """The library launches on the current HIP device: make it the tensors' device."""
+        import torch
+        _require(device.type == "cuda", f"tensors must be on a GPU, got {device}")
+        return torch.cuda.device(device)
 
     @staticmethod
     def _workspace(nbytes: int, device, workspace=None):
@@ -158,8 +177,10 @@ class Library:
     @staticmethod
     def _check_states(states, T: int):
         if states is not None:
-            assert states.is_contiguous() and states.numel() * states.element_size() >= T * 24
-            assert states.data_ptr() % 8 == 0
+            _require(states.is_contiguous() and
+                     states.numel() * states.element_size() >= T * ROW_STATE_BYTES,
+                     f"row_states must be contiguous with room for {T} x {ROW_STATE_BYTES} bytes")
+            _require(states.data_ptr() % 8 == 0, "row_states must be 8-byte aligned")
 
     @staticmethod
     def _ptr(t) -> int | None:
@@ -172,45 +193,50 @@ class Library:
         targets: [T] int64; row_states: optional [T * 24] uint8 tensor (fp32 logits only)
         that receives the rows' states for the backward call."""
         import torch
-        assert logits.dtype in (torch.float32, torch.bfloat16)
-        assert logits.dim() == 2 and logits.stride(1) == 1
-        assert targets.dtype == torch.int64 and targets.is_contiguous()
+        _require(logits.dtype in (torch.float32, torch.bfloat16), "logits must be fp32 or bf16")
+        _require(logits.dim() == 2 and logits.stride(1) == 1, "logits must be [T, V], unit stride")
+        _require(targets.dtype == torch.int64 and targets.is_contiguous(),
+                 "targets must be contiguous int64")
         T, V = logits.shape
         dev = logits.device
         lp, ent = out if out is not None else (
             torch.empty(T, dtype=torch.float32, device=dev),
             torch.empty(T, dtype=torch.float32, device=dev) if with_entropy else None)
-        ws, wsb = self._workspace(self.workspace_bytes(OP_FROM_LOGITS, T, V, 0, vocab_splits),
-                                  dev, workspace)
-        if logits.dtype == torch.float32:
-            self._check_states(row_states, T)
-            st = self.lib.rlk_logprob_from_logits(
-                self._ptr(logits), logits.stride(0), T, V, self._ptr(targets), temperature,
-                vocab_splits, self._ptr(lp), self._ptr(ent), self._ptr(row_states),
-                self._ptr(ws), wsb, self._stream_handle(stream))
-        else:
-            assert row_states is None, "row states are saved by the fp32 logits call only"
-            st = self.lib.rlk_logprob_from_logits_bf16(
-                self._ptr(logits), logits.stride(0), T, V, self._ptr(targets), temperature,
-                vocab_splits, self._ptr(lp), self._ptr(ent), self._ptr(ws), wsb,
-                self._stream_handle(stream))
+        _same_device(dev, targets, lp, ent, row_states, workspace)
+        with self._on(dev):
+            ws, wsb = self._workspace(self.workspace_bytes(OP_FROM_LOGITS, T, V, 0, vocab_splits),
+                                      dev, workspace)
+            if logits.dtype == torch.float32:
+                self._check_states(row_states, T)
+                st = self.lib.rlk_logprob_from_logits(
+                    self._ptr(logits), logits.stride(0), T, V, self._ptr(targets), temperature,
+                    vocab_splits, self._ptr(lp), self._ptr(ent), self._ptr(row_states),
+                    self._ptr(ws), wsb, self._stream_handle(stream, dev))
+            else:
+                _require(row_states is None, "row states are saved by the fp32 logits call only")
+                st = self.lib.rlk_logprob_from_logits_bf16(
+                    self._ptr(logits), logits.stride(0), T, V, self._ptr(targets), temperature,
+                    vocab_splits, self._ptr(lp), self._ptr(ent), self._ptr(ws), wsb,
+                    self._stream_handle(stream, dev))
         self.check(st, "rlk_logprob_from_logits")
         return lp, ent
 
     def entropy(self, logits, temperature: float = 1.0, vocab_splits: int = 1, out=None,
                 workspace=None, stream=None):
         import torch
-        assert logits.dtype in (torch.float32, torch.bfloat16)
-        assert logits.dim() == 2 and logits.stride(1) == 1
+        _require(logits.dtype in (torch.float32, torch.bfloat16), "logits must be fp32 or bf16")
+        _require(logits.dim() == 2 and logits.stride(1) == 1, "logits must be [T, V], unit stride")
         T, V = logits.shape
-        ent = out if out is not None else torch.empty(T, dtype=torch.float32,
-                                                      device=logits.device)
-        ws, wsb = self._workspace(self.workspace_bytes(OP_ENTROPY, T, V, 0, vocab_splits),
-                                  logits.device, workspace)
-        fn = self.lib.rlk_entropy if logits.dtype == torch.float32 else self.lib.rlk_entropy_bf16
-        st = fn(self._ptr(logits), logits.stride(0), T, V, temperature,
-                                  vocab_splits, self._ptr(ent), self._ptr(ws), wsb,
-                                  self._stream_handle(stream))
+        dev = logits.device
+        ent = out if out is not None else torch.empty(T, dtype=torch.float32, device=dev)
+        _same_device(dev, ent, workspace)
+        with self._on(dev):
+            ws, wsb = self._workspace(self.workspace_bytes(OP_ENTROPY, T, V, 0, vocab_splits),
+                                      dev, workspace)
+            fn = (self.lib.rlk_entropy if logits.dtype == torch.float32
+                  else self.lib.rlk_entropy_bf16)
+            st = fn(self._ptr(logits), logits.stride(0), T, V, temperature, vocab_splits,
+                    self._ptr(ent), self._ptr(ws), wsb, self._stream_handle(stream, dev))
         self.check(st, "rlk_entropy")
         return ent
 
@@ -219,27 +245,43 @@ class Library:
                        workspace=None, stream=None, row_states=None):
         """hidden: [T, d] bf16 (or int16/uint16 bits); weight: [V, d] same; targets [T] int64."""
         import torch
-        assert hidden.dim() == 2 and weight.dim() == 2
-        assert hidden.element_size() == 2 and weight.element_size() == 2
-        assert hidden.stride(1) == 1 and weight.stride(1) == 1
-        assert targets.dtype == torch.int64 and targets.is_contiguous()
+        self._check_operands(hidden, weight)
+        _require(targets.dtype == torch.int64 and targets.is_contiguous(),
+                 "targets must be contiguous int64")
         T, d = hidden.shape
-        V, d2 = weight.shape
-        assert d == d2
+        V = weight.shape[0]
         dev = hidden.device
         lp, ent = out if out is not None else (
             torch.empty(T, dtype=torch.float32, device=dev),
             torch.empty(T, dtype=torch.float32, device=dev) if with_entropy else None)
-        ws, wsb = self._workspace(self.workspace_bytes(OP_LINEAR, T, V, d, vocab_splits), dev,
-                                  workspace)
+        _same_device(dev, weight, targets, lp, ent, row_states, workspace)
         self._check_states(row_states, T)
-        st = self.lib.rlk_linear_logprob(
-            self._ptr(hidden), hidden.stride(0), self._ptr(weight), weight.stride(0), T, d, V,
-            self._ptr(targets), temperature, vocab_splits, self._ptr(lp), self._ptr(ent),
-            self._ptr(row_states), self._ptr(ws), wsb, self._stream_handle(stream))
+        with self._on(dev):
+            ws, wsb = self._workspace(self.workspace_bytes(OP_LINEAR, T, V, d, vocab_splits), dev,
+                                      workspace)
+            st = self.lib.rlk_linear_logprob(
+                self._ptr(hidden), hidden.stride(0), self._ptr(weight), weight.stride(0), T, d,
+                V, self._ptr(targets), temperature, vocab_splits, self._ptr(lp), self._ptr(ent),
+                self._ptr(row_states), self._ptr(ws), wsb, self._stream_handle(stream, dev))
         self.check(st, "rlk_linear_logprob")
         return lp, ent
 
+    @staticmethod
+    def _check_operands(hidden, weight):
+        _require(hidden.dim() == 2 and weight.dim() == 2, "hidden and weight must be 2-D")
+        _require(hidden.element_size() == 2 and weight.element_size() == 2,
+                 "hidden and weight must hold bf16 (2-byte) elements")
+        _require(hidden.stride(1) == 1 and weight.stride(1) == 1,
+                 "hidden and weight must have unit column stride")
+        _require(hidden.shape[1] == weight.shape[1], "hidden and weight disagree on hidden_dim")
+
+    @staticmethod
+    def _check_row_grads(T: int, *grads):
+        import torch
+        for g in grads:
+            _require(g is None or (g.dtype == torch.float32 and tuple(g.shape) == (T,) and
+                                   g.is_contiguous()),
+                     "upstream gradients must be contiguous fp32 [T]")
 
     def logprob_backward_from_logits(self, logits, targets, temperature: float = 1.0,
                                      vocab_splits: int = 1, grad_logprob=None, grad_entropy=None,
@@ -247,24 +289,27 @@ class Library:
         """Gradient of sum g_lp * logprob + g_ent * entropy w.r.t. fp32 logits [T, >=V];
         returns `out` (new [T, V] fp32 tensor if None; may be `logits` itself)."""
         import torch
-        assert logits.dtype == torch.float32 and logits.dim() == 2 and logits.stride(1) == 1
+        _require(logits.dtype == torch.float32 and logits.dim() == 2 and logits.stride(1) == 1,
+                 "logits must be fp32 [T, V] with unit column stride")
         T, V = logits.shape
-        for g in (grad_logprob, grad_entropy):
-            assert g is None or (g.dtype == torch.float32 and g.shape == (T,) and
-                                 g.is_contiguous())
+        dev = logits.device
+        self._check_row_grads(T, grad_logprob, grad_entropy)
         if targets is not None:
-            assert targets.dtype == torch.int64 and targets.is_contiguous()
-        grad = out if out is not None else torch.empty((T, V), dtype=torch.float32,
-                                                       device=logits.device)
-        assert grad.dtype == torch.float32 and grad.stride(1) == 1 and grad.shape == (T, V)
+            _require(targets.dtype == torch.int64 and targets.is_contiguous(),
+                     "targets must be contiguous int64")
+        grad = out if out is not None else torch.empty((T, V), dtype=torch.float32, device=dev)
+        _require(grad.dtype == torch.float32 and grad.stride(1) == 1 and
+                 tuple(grad.shape) == (T, V), "out must be fp32 [T, V] with unit column stride")
+        _same_device(dev, targets, grad_logprob, grad_entropy, grad, row_states, workspace)
         self._check_states(row_states, T)
-        ws, wsb = self._workspace(self.workspace_bytes(OP_BACKWARD_FROM_LOGITS, T, V, 0,
-                                                       vocab_splits), logits.device, workspace)
-        st = self.lib.rlk_logprob_backward_from_logits(
-            self._ptr(logits), logits.stride(0), T, V, self._ptr(targets), temperature,
-            vocab_splits, self._ptr(grad_logprob), self._ptr(grad_entropy),
-            self._ptr(row_states), self._ptr(grad), grad.stride(0), self._ptr(ws), wsb,
-            self._stream_handle(stream))
+        with self._on(dev):
+            ws, wsb = self._workspace(self.workspace_bytes(OP_BACKWARD_FROM_LOGITS, T, V, 0,
+                                                           vocab_splits), dev, workspace)
+            st = self.lib.rlk_logprob_backward_from_logits(
+                self._ptr(logits), logits.stride(0), T, V, self._ptr(targets), temperature,
+                vocab_splits, self._ptr(grad_logprob), self._ptr(grad_entropy),
+                self._ptr(row_states), self._ptr(grad), grad.stride(0), self._ptr(ws), wsb,
+                self._stream_handle(stream, dev))
         self.check(st, "rlk_logprob_backward_from_logits")
         return grad
 
@@ -275,31 +320,36 @@ class Library:
         """Gradients (dH [T, d], dW [V, d], fp32; None where not requested) of
         sum g_lp * logprob + g_ent * entropy for logits = hidden @ weight^T (bf16 bits)."""
         import torch
-        assert hidden.dim() == 2 and weight.dim() == 2
-        assert hidden.element_size() == 2 and weight.element_size() == 2
-        assert hidden.stride(1) == 1 and weight.stride(1) == 1
+        self._check_operands(hidden, weight)
         T, d = hidden.shape
-        V, d2 = weight.shape
-        assert d == d2
+        V = weight.shape[0]
         dev = hidden.device
-        for g in (grad_logprob, grad_entropy):
-            assert g is None or (g.dtype == torch.float32 and g.shape == (T,) and
-                                 g.is_contiguous())
+        self._check_row_grads(T, grad_logprob, grad_entropy)
+        if targets is not None:
+            _require(targets.dtype == torch.int64 and targets.is_contiguous(),
+                     "targets must be contiguous int64")
         if out is not None:
             dh, dw = out
         else:
             dh = torch.empty((T, d), dtype=torch.float32, device=dev) if need_hidden else None
             dw = torch.empty((V, d), dtype=torch.float32, device=dev) if need_weight else None
+        for g, shape in ((dh, (T, d)), (dw, (V, d))):
+            _require(g is None or (g.dtype == torch.float32 and tuple(g.shape) == shape and
+                                   g.stride(1) == 1),
+                     f"gradient outputs must be fp32 {shape} with unit column stride")
+        _same_device(dev, weight, targets, grad_logprob, grad_entropy, row_states, dh, dw,
+                     workspace)
         self._check_states(row_states, T)
-        ws, wsb = self._workspace(self.workspace_bytes(OP_LINEAR_BACKWARD, T, V, d, vocab_splits),
-                                  dev, workspace)
-        st = self.lib.rlk_linear_logprob_backward(
-            self._ptr(hidden), hidden.stride(0), self._ptr(weight), weight.stride(0), T, d, V,
-            self._ptr(targets), temperature, vocab_splits, self._ptr(grad_logprob),
-            self._ptr(grad_entropy), self._ptr(row_states), self._ptr(dh),
-            dh.stride(0) if dh is not None else 0,
-            self._ptr(dw), dw.stride(0) if dw is not None else 0, self._ptr(ws), wsb,
-            self._stream_handle(stream))
+        with self._on(dev):
+            ws, wsb = self._workspace(self.workspace_bytes(OP_LINEAR_BACKWARD, T, V, d,
+                                                           vocab_splits), dev, workspace)
+            st = self.lib.rlk_linear_logprob_backward(
+                self._ptr(hidden), hidden.stride(0), self._ptr(weight), weight.stride(0), T, d,
+                V, self._ptr(targets), temperature, vocab_splits, self._ptr(grad_logprob),
+                self._ptr(grad_entropy), self._ptr(row_states), self._ptr(dh),
+                dh.stride(0) if dh is not None else 0,
+                self._ptr(dw), dw.stride(0) if dw is not None else 0, self._ptr(ws), wsb,
+                self._stream_handle(stream, dev))
         self.check(st, "rlk_linear_logprob_backward")
         return dh, dw
 
@@ -307,19 +357,25 @@ class Library:
                               stream=None):
         """Launch rlk_logprob_compare; returns the 64-byte device result tensor (uint8)."""
         import torch
-        assert train.dtype == torch.float32 and rollout.dtype == torch.float32
-        assert train.dim() == 1 and train.shape == rollout.shape
-        assert train.is_contiguous() and rollout.is_contiguous()
+        _require(train.dtype == torch.float32 and rollout.dtype == torch.float32,
+                 "logprobs must be fp32")
+        _require(train.dim() == 1 and train.shape == rollout.shape, "logprobs must be [T] alike")
+        _require(train.is_contiguous() and rollout.is_contiguous(), "logprobs must be contiguous")
         if mask is not None:
-            assert mask.dtype in (torch.uint8, torch.bool) and mask.shape == train.shape
-            assert mask.is_contiguous()
+            _require(mask.dtype in (torch.uint8, torch.bool) and mask.shape == train.shape and
+                     mask.is_contiguous(), "mask must be a contiguous [T] bool or uint8 tensor")
         T = train.shape[0]
-        res = out if out is not None else torch.empty(64, dtype=torch.uint8, device=train.device)
-        wsb = self.workspace_bytes(OP_COMPARE, T, 1)
-        ws, wsb = self._workspace(wsb, train.device, workspace)
-        st = self.lib.rlk_logprob_compare(self._ptr(train), self._ptr(rollout), self._ptr(mask),
-                                          T, self._ptr(res), self._ptr(ws), wsb,
-                                          self._stream_handle(stream))
+        dev = train.device
+        res = out if out is not None else torch.empty(64, dtype=torch.uint8, device=dev)
+        _require(res.numel() * res.element_size() >= 64 and res.is_contiguous(),
+                 "out must hold 64 contiguous bytes")
+        _same_device(dev, rollout, mask, res, workspace)
+        with self._on(dev):
+            wsb = self.workspace_bytes(OP_COMPARE, T, 1)
+            ws, wsb = self._workspace(wsb, dev, workspace)
+            st = self.lib.rlk_logprob_compare(self._ptr(train), self._ptr(rollout),
+                                              self._ptr(mask), T, self._ptr(res), self._ptr(ws),
+                                              wsb, self._stream_handle(stream, dev))
         self.check(st, "rlk_logprob_compare")
         return res
 
