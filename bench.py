@@ -13,7 +13,9 @@ Also reported on the same JSON line:
   cpu_baseline  the float64 CPU oracle on the same rows;
   fused         the fused linear-logp path on the Qwen3-8B shape (T = 2048, d = 4096,
                 V = 151936 bf16) as tokens/s and fraction of the 2.5 PFLOP/s bf16
-                MFMA peak (2 T V d flops per call);
+                MFMA peak (2 T V d flops per call); fused.configs adds the Qwen3-Next
+                shape (T = 1024, d = 2048) and the large ragged batch (T = 16384,
+                d = 4096, temperature 0.7);
   splits        ms per call of the logits path at vocab splits 2, 4, 8;
   bf16_logits   the same rows rounded to bf16 through rlk_logprob_from_logits_bf16
                 (1024 x 303888 B per call) as GB/s against 8 TB/s;
@@ -93,6 +95,24 @@ def time_calls(fn, steps: int, warmup: int):
     return start.elapsed_time(end) / steps, wall_ms / steps
 
 
+def fused_config_rate(lib, h, w, t, tau, steps, warmup):
+    """ms per rlk_linear_logprob call and fraction of the bf16 MFMA peak on one shape."""
+    import torch
+    from entropy_rlk_logprob_amd import binding
+    T, d = h.shape
+    V = w.shape[0]
+    lp = torch.empty(T, dtype=torch.float32, device="cuda")
+    ent = torch.empty(T, dtype=torch.float32, device="cuda")
+    ws = torch.empty(lib.workspace_bytes(binding.OP_LINEAR, T, V, d, 1), dtype=torch.uint8,
+                     device="cuda")
+    log(f"timing fused path T={T} d={d}: steps {steps}")
+    ms, _ = time_calls(lambda: lib.linear_logprob(h, w, t, tau, 1, out=(lp, ent), workspace=ws),
+                       steps, warmup)
+    tf = 2.0 * T * V * d / (ms / 1e3) / 1e12
+    return {"n_tokens": T, "hidden": d, "temperature": tau, "ms_per_call": round(ms, 4),
+            "tokens_per_s": round(T / (ms / 1e3), 1), "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+
+
 def cpu_baseline(case):
     import oracle
     t0 = time.perf_counter()
@@ -110,6 +130,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-fused", action="store_true")
+    ap.add_argument("--no-fused-configs", action="store_true",
+                    help="skip the T=1024 d=2048 and T=16384 d=4096 fused shapes")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run 5 device-to-device copies of the logits tensor (a plain copy of "
@@ -261,7 +283,30 @@ def main():
                               "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                               "flops_per_call": flops}}
-        del h, w
+        fused_configs = {S.WORKLOADS[4].name: {"ms_per_call": fused["ms_per_call"],
+                                               "frac": fused["roofline"]["frac"]}}
+        if not args.no_fused_configs:
+            # The other two fused shapes.  T = 16384 reuses the W just timed (same shape and
+            # distribution as its own) and takes uniform targets: neither changes the work.
+            log("generating fused workload T=16384 d=4096 (H only)")
+            w5 = S.WORKLOADS[5]
+            st5 = S.streams(S.cfg_seed(5))
+            h5 = torch.from_numpy(S.to_bf16_bits(S.normal_f32(
+                st5[S.STREAM_X], (w5.n_tokens, w5.hidden), w5.sigma)).view(np.int16)).cuda()
+            t5 = torch.from_numpy(S.uniform_targets(st5[S.STREAM_TARGET], w5.n_tokens,
+                                                    V)).cuda()
+            fused_configs[w5.name] = fused_config_rate(lib, h5, w, t5, w5.temperature, 3, 1)
+            del h5, t5
+            del w
+            log("generating fused workload T=1024 d=2048 V=151936 (bf16)")
+            fc3 = S.fused_workload(3)
+            h3 = torch.from_numpy(fc3.h_bits.view(np.int16)).cuda()
+            w3 = torch.from_numpy(fc3.w_bits.view(np.int16)).cuda()
+            t3 = torch.from_numpy(fc3.targets).cuda()
+            fused_configs[S.WORKLOADS[3].name] = fused_config_rate(lib, h3, w3, t3, 1.0, 20, 3)
+            del h3, w3, t3
+        fused["configs"] = fused_configs
+        del h
 
     cpu = None if args.no_cpu else cpu_baseline(case)
 
