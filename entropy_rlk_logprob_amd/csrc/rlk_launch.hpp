@@ -79,13 +79,12 @@ hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream);
 // Fused-path backward (rlk_linear_bwd.hip).  Workspace: the forward layout, then the
 // regions below (byte offsets from the workspace base).
 struct LinearBackwardWorkspace {
-  int64_t Vp, Tp;  // V and T rounded up to multiples of 64 (K padding of the NT GEMMs)
+  int64_t Vp, Tp;  // V and T rounded up to multiples of 64 (K padding of the GEMMs)
   size_t root;     // T root states
   size_t rowc;     // T per-token gradient constants
-  size_t wt;       // W^T [d, Vp] bf16
   size_t ht;       // H^T [d, Tp] bf16
-  size_t dx;       // dX [T, Vp] bf16
-  size_t dxt;      // dX^T [V, Tp] bf16
+  size_t dx;       // dX [T, Vp] bf16, zero in columns [V, Vp)
+  size_t dxt;      // dX^T [V, Tp] bf16, zero in columns [T, Tp)
   size_t part;     // 8 split-K partials of dH [T, d] fp32
   size_t total;
 };

@@ -12,12 +12,14 @@
 //      skipped when the caller passes the states its forward call saved;
 //   2. per-token constants (m, log2 s, entropy, upstream gradients, target, row mode);
 //   3. the logits tile is recomputed on MFMA (same tile loop and K order as the forward)
-//      and its gradient dX is written in bf16, row-major [T, Vp] and transposed [V, Tp];
-//   4. W^T [d, Vp] and H^T [d, Tp] (bf16 transposes, zero padding on K);
-//   5. dH^T = W^T . dX^T as an NT GEMM (both operands K-contiguous), K = Vp split into 8
-//      fixed ranges (boundaries depend on V only), partials summed in the fixed tree
-//      ((0,1),(2,3)),((4,5),(6,7));
-//   6. dW = dX^T . H as an NT GEMM, K = Tp in one increasing-order pass per output tile.
+//      and its gradient dX is written in bf16, row-major [T, Vp] (for dH) and transposed
+//      [V, Tp] (for dW), with zero K padding;
+//   4. dH = dX . W on the shared tile loop, dX K-contiguous and W read in place as a
+//      K-major operand (gfx950 LDS transpose loads, so no transposed copy of W is made);
+//      K = Vp split into 8 fixed ranges (boundaries depend on V only), partials summed in
+//      the fixed tree ((0,1),(2,3)),((4,5),(6,7));
+//   5. dW = dX^T . H with dX^T and a transposed copy of H (small), K = Tp in one
+//      increasing-order pass per output tile.
 // A token's row of dH depends only on that token (its place among the GEMM's columns does
 // not change the accumulation order), so dH is batch-invariant like the forward; dW sums
 // over the batch in increasing token order.
@@ -168,7 +170,8 @@ __global__ __launch_bounds__(kThreads, 1) void dx_tile_kernel(
   }
 }
 
-// Step 4: out[c][r] = in[r][c] for r < R, c < C; out[c][r] = 0 for R <= r < Rp.
+// H^T for the dW contraction: out[c][r] = in[r][c] for r < R, c < C; out[c][r] = 0 for
+// R <= r < Rp.
 // 64 x 64 tiles through LDS; each lane moves 16 contiguous bytes (8 elements) per global
 // access when the row strides and the tile allow it (the common case), else elements.
 __global__ __launch_bounds__(256) void transpose_pad_kernel(
@@ -221,7 +224,7 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(
   }
 }
 
-// Zero columns [c_begin, c_end) of rows [0, rows) of a bf16 matrix (K padding of dX, dX^T).
+// Zero columns [c_begin, c_end) of rows [0, rows) of a bf16 matrix (the padding of dX).
 __global__ __launch_bounds__(256) void zero_cols_kernel(uint16_t* __restrict__ p, int64_t ld,
                                                         int64_t rows, int64_t c_begin,
                                                         int64_t c_end) {
@@ -231,18 +234,24 @@ __global__ __launch_bounds__(256) void zero_cols_kernel(uint16_t* __restrict__ p
     p[(i / width) * ld + c_begin + i % width] = 0;
 }
 
-// Steps 5 and 6: C(m, n) = sum_k A[m, k] B[n, k] over the split's K range, in 256 x 256
-// tiles on the shared MFMA loop.  TRANS: stored at C[n * ldc + m] (4 consecutive m per
-// 16-byte store), else at C[m * ldc + n].  Split s (blockIdx.y) covers K steps
+// Steps 4 and 5: C(m, n) = sum_k A[m, k] B[n, k] over the split's K range, in 256 x 256
+// tiles on the shared MFMA loop.  An operand is K-contiguous ([rows, K], row r at
+// X + r ld) or K-major ([K, rows], k row at X + k ld; its k rows beyond k_last are
+// clamped, the other operand holding zeros there).  Stored row-major at C[m * ldc + n]
+// (32 lanes write 128 contiguous bytes of a row).  Split s (blockIdx.y) covers K steps
 // [s * steps, (s + 1) * steps) and writes C + s * split_stride; an empty range writes 0.
-template <bool TRANS>
-__global__ __launch_bounds__(kThreads, 1) void nt_gemm_kernel(
-    const uint16_t* __restrict__ A, int64_t lda, int64_t M, const uint16_t* __restrict__ B,
-    int64_t ldb, int64_t N, int64_t K, int64_t steps, float* __restrict__ C, int64_t ldc,
-    int64_t split_stride) {
+// SHARE_B: tiles are taken column-tile-major (consecutive logical tiles share a B slice),
+// else row-tile-major (they share an A slice): the larger operand is fetched from HBM once
+// and shared in an XCD's L2.
+template <bool A_KMAJOR, bool B_KMAJOR, bool SHARE_B>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, int64_t M, int64_t a_klast,
+    const uint16_t* __restrict__ B, int64_t ldb, int64_t N, int64_t b_klast, int64_t K,
+    int64_t steps, float* __restrict__ C, int64_t ldc, int64_t split_stride) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
   int64_t mt, nt;
-  if (!tile_of((M + kTile - 1) / kTile, (N + kTile - 1) / kTile, mt, nt)) return;
+  const int64_t n_mt = (M + kTile - 1) / kTile, n_nt = (N + kTile - 1) / kTile;
+  if (!(SHARE_B ? tile_of(n_nt, n_mt, nt, mt) : tile_of(n_mt, n_nt, mt, nt))) return;
   const int64_t m_lo = mt * kTile, n_lo = nt * kTile;
   const int64_t k_begin = (int64_t)blockIdx.y * steps * kBK;
   const int64_t k_end = min(k_begin + steps * kBK, K);
@@ -254,9 +263,13 @@ __global__ __launch_bounds__(kThreads, 1) void nt_gemm_kernel(
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
-  if (nk > 0)
-    mma::mma_tile(A + m_lo * lda, lda, (int)min((int64_t)kTile, M - m_lo) - 1, B + n_lo * ldb, ldb,
-                  (int)min((int64_t)kTile, N - n_lo) - 1, k_begin, nk, smem, acc);
+  if (nk > 0) {
+    const int a_last = (int)min((int64_t)kTile, M - m_lo) - 1;
+    const int b_last = (int)min((int64_t)kTile, N - n_lo) - 1;
+    const mma::Operand Aop{A_KMAJOR ? A + m_lo : A + m_lo * lda, lda, a_last, a_klast};
+    const mma::Operand Bop{B_KMAJOR ? B + n_lo : B + n_lo * ldb, ldb, b_last, b_klast};
+    mma::mma_tile_op<A_KMAJOR, B_KMAJOR>(Aop, Bop, k_begin, nk, smem, acc);
+  }
   float* __restrict__ Cs = C + (int64_t)blockIdx.y * split_stride;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -272,20 +285,9 @@ __global__ __launch_bounds__(kThreads, 1) void nt_gemm_kernel(
       for (int g4 = 0; g4 < 4; ++g4) {
         const int64_t m0 = m_lo + wv * 128 + a * 32 + 8 * g4 + 4 * fhalf;
         if (m0 >= M) continue;
-        if constexpr (TRANS) {
-          float* dst = Cs + n * ldc + m0;
-          if (m0 + 4 <= M) {
-            *reinterpret_cast<float4*>(dst) =
-                make_float4(acc[a][b][4 * g4], acc[a][b][4 * g4 + 1], acc[a][b][4 * g4 + 2],
-                            acc[a][b][4 * g4 + 3]);
-          } else {
-            for (int j = 0; j < 4 && m0 + j < M; ++j) dst[j] = acc[a][b][4 * g4 + j];
-          }
-        } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (m0 + j < M) Cs[(m0 + j) * ldc + n] = acc[a][b][4 * g4 + j];
-        }
+        for (int j = 0; j < 4; ++j)
+          if (m0 + j < M) Cs[(m0 + j) * ldc + n] = acc[a][b][4 * g4 + j];
       }
     }
   }
@@ -326,8 +328,6 @@ LinearBackwardWorkspace linear_backward_layout(int64_t T, int64_t V, int64_t d, 
   off += align256((size_t)T * sizeof(WireState));
   L.rowc = off;
   off += align256((size_t)T * sizeof(GradRowC));
-  L.wt = off;
-  off += align256((size_t)d * (size_t)L.Vp * 2);
   L.ht = off;
   off += align256((size_t)d * (size_t)L.Tp * 2);
   L.dx = off;
@@ -360,25 +360,17 @@ hipError_t launch_linear_backward(const LinearArgs& fwd, const float* g_lp, cons
                      states ? states : a.root, T, V, a.targets, g_lp, g_ent, a.beta, rc);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  uint16_t* wt = reinterpret_cast<uint16_t*>(base + L.wt);
-  uint16_t* ht = reinterpret_cast<uint16_t*>(base + L.ht);
+  // Step 3 writes dX [T, Vp] (for dH) and dX^T [V, Tp] (for dW); their K padding
+  // (columns [V, Vp), resp. [T, Tp)) is zeroed here, so the contractions see zeros there.
   uint16_t* dx = dH ? reinterpret_cast<uint16_t*>(base + L.dx) : nullptr;
   uint16_t* dxt = dW ? reinterpret_cast<uint16_t*>(base + L.dxt) : nullptr;
   const unsigned fill_blocks = 2048;
-  if (dH) {
-    hipLaunchKernelGGL(transpose_pad_kernel, dim3((unsigned)(L.Vp / 64), (unsigned)(d / 64)),
-                       dim3(256), 0, stream, a.W, a.ldw, V, d, wt, L.Vp, L.Vp);
-    if (L.Vp > V)
-      hipLaunchKernelGGL(zero_cols_kernel, dim3(fill_blocks), dim3(256), 0, stream, dx, L.Vp, T, V,
-                         L.Vp);
-  }
-  if (dW) {
-    hipLaunchKernelGGL(transpose_pad_kernel, dim3((unsigned)(L.Tp / 64), (unsigned)(d / 64)),
-                       dim3(256), 0, stream, a.H, a.ldh, T, d, ht, L.Tp, L.Tp);
-    if (L.Tp > T)
-      hipLaunchKernelGGL(zero_cols_kernel, dim3(fill_blocks), dim3(256), 0, stream, dxt, L.Tp, V,
-                         T, L.Tp);
-  }
+  if (dx && L.Vp > V)
+    hipLaunchKernelGGL(zero_cols_kernel, dim3(fill_blocks), dim3(256), 0, stream, dx, L.Vp, T, V,
+                       L.Vp);
+  if (dxt && L.Tp > T)
+    hipLaunchKernelGGL(zero_cols_kernel, dim3(fill_blocks), dim3(256), 0, stream, dxt, L.Tp, V,
+                       T, L.Tp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   const int64_t tiles_x = ((V + kTile - 1) / kTile) * ((T + kTile - 1) / kTile);
@@ -387,13 +379,16 @@ hipError_t launch_linear_backward(const LinearArgs& fwd, const float* g_lp, cons
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   if (dH) {
-    // dH^T[k, t] = sum_v W^T[k, v] dX[t, v]: A = W^T (M = d), B = dX (N = T), K = Vp.
+    // dH[t, k] = sum_v dX[t, v] W[v, k]: A = dX K-contiguous (M = T), B = W read in place
+    // as a K-major operand (N = d; k rows v clamped to V - 1, where dX is zero), K = Vp;
+    // column-tile-major so that the tiles sharing a W slice run together.
     float* part = reinterpret_cast<float*>(base + L.part);
     const int64_t steps = (L.Vp / kBK + kDhSplits - 1) / kDhSplits;
-    const int64_t tiles = ((d + kTile - 1) / kTile) * ((T + kTile - 1) / kTile);
-    hipLaunchKernelGGL((nt_gemm_kernel<true>), dim3((unsigned)((tiles + 7) / 8 * 8), kDhSplits),
-                       dim3(kThreads), 0, stream, wt, L.Vp, d, dx, L.Vp, T, L.Vp, steps, part, d,
-                       T * d);
+    const int64_t tiles = ((T + kTile - 1) / kTile) * ((d + kTile - 1) / kTile);
+    hipLaunchKernelGGL((gemm_kernel<false, true, true>),
+                       dim3((unsigned)((tiles + 7) / 8 * 8), kDhSplits), dim3(kThreads), 0,
+                       stream, dx, L.Vp, T, (int64_t)0, a.W, a.ldw, d, V - 1, L.Vp, steps, part,
+                       d, T * d);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t nq = T * (d / 4);
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0,
@@ -401,11 +396,20 @@ hipError_t launch_linear_backward(const LinearArgs& fwd, const float* g_lp, cons
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (dW) {
-    // dW[v, k] = sum_t dX^T[v, t] H^T[k, t]: A = dX^T (M = V), B = H^T (N = d), K = Tp.
+    // dW[v, k] = sum_t dX^T[v, t] H^T[k, t]: A = dX^T (M = V), B = H^T (N = d; a transposed
+    // copy of H, small), both K-contiguous, K = Tp; row-tile-major so that the tiles
+    // sharing a dX^T slice run together; stored row-major (32 lanes write 128 contiguous
+    // bytes of a dW row).  (Reading dX in place as a K-major A operand measured 0.6 ms
+    // slower at T = 2048, d = 4096, V = 151936 than writing dX^T in step 3.)
+    uint16_t* ht = reinterpret_cast<uint16_t*>(base + L.ht);
+    hipLaunchKernelGGL(transpose_pad_kernel, dim3((unsigned)(L.Tp / 64), (unsigned)(d / 64)),
+                       dim3(256), 0, stream, a.H, a.ldh, T, d, ht, L.Tp, L.Tp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t tiles = ((V + kTile - 1) / kTile) * ((d + kTile - 1) / kTile);
-    hipLaunchKernelGGL((nt_gemm_kernel<false>), dim3((unsigned)((tiles + 7) / 8 * 8), 1),
-                       dim3(kThreads), 0, stream, dxt, L.Tp, V, ht, L.Tp, d, L.Tp,
-                       L.Tp / kBK, dW, ld_dw, (int64_t)0);
+    hipLaunchKernelGGL((gemm_kernel<false, false, false>),
+                       dim3((unsigned)((tiles + 7) / 8 * 8), 1), dim3(kThreads), 0, stream, dxt,
+                       L.Tp, V, (int64_t)0, ht, L.Tp, d, (int64_t)0, L.Tp, L.Tp / kBK, dW, ld_dw,
+                       (int64_t)0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

@@ -1,20 +1,25 @@
-// 256 x 256 bf16 MFMA output tile with K-contiguous operands, shared by the fused
-// forward, the logit-gradient recompute and the NT GEMMs of the fused backward:
+// 256 x 256 bf16 MFMA output tile, shared by the fused forward, the logit-gradient
+// recompute and the GEMMs of the fused backward:
 //   acc(r, c) += sum_k A[r, k] B[c, k]   over k in [k0, k0 + 64 nk),
 // A rows r = 0..255 of the tile ("A side", e.g. vocabulary rows of W), B rows c = 0..255
-// ("B side", e.g. tokens of H), both row-major with K contiguous.
+// ("B side", e.g. tokens of H).  Each operand is either K-contiguous (row-major [rows, K],
+// the layout of W and H in the forward) or K-major (row-major [K, rows], e.g. W read as
+// the operand of dH = dX W): the latter is staged as is and its MFMA fragments are read
+// with the LDS transpose load, so no transposed copy is ever written.
 //
 // Workgroup: 8 waves arranged 2 (A side) x 4 (B side), each wave 128 x 64 = 4 x 2 MFMA
 // blocks (v_mfma_f32_32x32x16_bf16).  Accumulation order of every output: 64-wide K steps
 // in increasing order, each four MFMA steps of 16 consecutive k -- independent of the
-// output's place in the tile.  Output layout: lane l of wave (wa, wb) holds, in
-// acc[a][b][i], row wa*128 + a*32 + 8*(i/4) + 4*(l/32) + (i%4) and column
-// wb*64 + b*32 + (l%32).
+// output's place in the tile and of the operands' layouts.  Output layout: lane l of wave
+// (wa, wb) holds, in acc[a][b][i], row wa*128 + a*32 + 8*(i/4) + 4*(l/32) + (i%4) and
+// column wb*64 + b*32 + (l%32).
 //
-// LDS: two 64 KiB stages of (256 + 256) rows x 64 bf16, each 128-byte row with an XOR
-// swizzle on its 16-byte columns so that ds_read_b128 of 16 consecutive rows hits
-// distinct banks.  Global -> LDS by direct LDS-DMA loads (global_load_lds_dwordx4), issued
-// one stage ahead.
+// LDS: two 64 KiB stages, each an A slab and a B slab of 32 KiB (256 rows x 64 k).  A
+// K-contiguous slab holds 128-byte rows (64 k) with an XOR swizzle on their 16-byte
+// columns so that ds_read_b128 of 16 consecutive rows hits distinct banks; a K-major slab
+// holds 512-byte rows (one k, 256 tile rows) swizzled so that the four k rows one
+// transpose load touches fall in four different bank groups.  Global -> LDS by direct
+// LDS-DMA loads (global_load_lds_dwordx4), issued one stage ahead.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -59,62 +64,140 @@ __device__ __forceinline__ int lds_offset(int row, int c16) {
   return row * 128 + ((c16 ^ ((row >> 1) & 7)) << 4);
 }
 
+// K-major slab layout: row k of 256 bf16 = 512 bytes; 16-byte column c of row k sits at
+// physical column c ^ (4 (k % 4)), i.e. rows k = 0..3 (mod 4) are rotated by 64 bytes
+// against each other.
+__device__ __forceinline__ int lds_offset_kmajor(int k, int col) {  // col: element, % 4 == 0
+  return k * 512 + ((((col >> 3) ^ ((k & 3) << 2))) << 4) + ((col & 4) << 1);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// gfx950 LDS transpose load (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane j
+// supplies the address of 4 consecutive 16-bit elements, and lane i receives element
+// i % 4 of the chunks of lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4, in that order
+// (a 16 x 4 -> 4 x 16 transpose; verified on the device).  So if lane 4e + q points at
+// k row kb + e, columns cb + 4q .. cb + 4q + 3, lane i receives column cb + i at rows
+// kb .. kb + 3.
+__device__ __forceinline__ v4i16 ds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(const_cast<char*>(p)));
+}
+
+// One MFMA operand fragment (rows base .. base + 31 of the slab, k 16 ks .. 16 ks + 15):
+// lane l holds row base + l % 32, k = 16 ks + 8 (l / 32) + j, j = 0..7.
+template <bool KMAJOR>
+__device__ __forceinline__ bf16x8 read_fragment(const char* slab, int base, int ks) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (!KMAJOR) {
+    const int c16 = 2 * ks + (lane >> 5);
+    return __builtin_bit_cast(bf16x8,
+                              *reinterpret_cast<const U4*>(slab + lds_offset(base + (lane & 31),
+                                                                             c16)));
+  } else {
+    // Group g = l / 16 covers rows base + 16 (g % 2) + 0..15 at k 16 ks + 8 (g / 2) + 0..7,
+    // in two transpose loads of four k each.
+    const int g = lane >> 4, i = lane & 15;
+    const int k = 16 * ks + 8 * (g >> 1) + (i >> 2);
+    const int col = base + 16 * (g & 1) + 4 * (i & 3);
+    const v4i16 lo = ds_read_tr16(slab + lds_offset_kmajor(k, col));
+    const v4i16 hi = ds_read_tr16(slab + lds_offset_kmajor(k + 4, col));
+    const v4i16 both[2] = {lo, hi};
+    return __builtin_bit_cast(bf16x8, both);
+  }
+}
+
+// Scheduling groups spreading kReads LDS reads over six MFMAs (as evenly as possible).
+template <int kReads, int Q>
+__device__ __forceinline__ void sched_reads_over_mfmas() {
+  if constexpr (Q < 6) {
+    constexpr int n = kReads * (Q + 1) / 6 - kReads * Q / 6;
+    sched_group(kSchedMfma, 1);
+    if constexpr (n > 0) sched_group(kSchedDsRead, n);
+    sched_reads_over_mfmas<kReads, Q + 1>();
+  }
+}
+
+// An operand of the tile: K-contiguous ([rows, K], row r at p + r ld) or K-major
+// ([K, rows], k row at p + k ld).
+//   p      element (row 0 of the tile, k = 0)
+//   ld     stride (elements) between rows (K-contiguous) or between k rows (K-major)
+//   last   last valid row of the tile (rows beyond are clamped to it; the caller must not
+//          use their outputs); K-major: last + 1 must be a multiple of 8
+//   k_last K-major only: last k row that may be read (k rows beyond are clamped to it; the
+//          other operand must hold zeros there)
+struct Operand {
+  const uint16_t* p;
+  int64_t ld;
+  int last;
+  int64_t k_last;
+};
+
 // Runs the K loop; the caller zeroes acc and, after the return (which waits for the
 // last DMA), issues a workgroup barrier before reusing smem.
-//   At, Bt       first row of the tile's A / B rows (element 0 of K)
-//   lda, ldb     row strides (elements)
-//   a_last, b_last  last valid row index within the tile (rows beyond are clamped to it;
-//                the caller must not use their outputs)
-//   k0, nk       first K element (multiple of 8) and number of 64-wide K steps (>= 1)
-__device__ __forceinline__ void mma_tile(const uint16_t* __restrict__ At, int64_t lda,
-                                         int a_last, const uint16_t* __restrict__ Bt,
-                                         int64_t ldb, int b_last, int64_t k0, int nk, char* smem,
-                                         floatx16 (&acc)[4][2]) {
+//   k0, nk  first K element (multiple of 8) and number of 64-wide K steps (>= 1)
+template <bool A_KMAJOR, bool B_KMAJOR>
+__device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, int64_t k0,
+                                            int nk, char* smem, floatx16 (&acc)[4][2]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wv = wave >> 2;  // A-side half (0, 1)
   const int wt = wave & 3;   // B-side quarter (0..3)
-  const uint16_t* __restrict__ Wt = At + k0;
-  const uint16_t* __restrict__ Ht = Bt + k0;
-  const int w_last = a_last;
-  const int h_last = b_last;
-  const int64_t ldw = lda;
-  const int64_t ldh = ldb;
-  // Global -> LDS: direct 16-byte-per-lane loads into LDS (global_load_lds_dwordx4).  One
-  // wave instruction fills one 1 KiB block = 8 slab rows: lane l writes physical column
-  // l % 8 of row r = 8 b + l / 8 of block b, so it fetches logical column
-  // (l % 8) ^ ((r / 2) % 8), the layout of lds_offset().  Blocks 0..31 are the A slab,
-  // 32..63 the B slab; wave w fills blocks w, w + 8, ..., w + 56.  Offsets are
-  // tile-relative on workgroup-uniform bases; rows beyond the valid range are clamped to
-  // the last valid row (their values are masked in the epilogue or never stored).
+  // Global -> LDS: direct 16-byte-per-lane loads into LDS (global_load_lds_dwordx4); one
+  // wave instruction fills one 1 KiB block with lane l's 16 bytes at byte 16 l.  Blocks
+  // 0..31 are the A slab, 32..63 the B slab; wave w fills blocks w, w + 8, ..., w + 56.
+  //   K-contiguous: a block is 8 slab rows of 128 bytes; lane l writes physical column
+  //     l % 8 of row 8 b + l / 8 and so fetches logical column (l % 8) ^ ((row / 2) % 8).
+  //   K-major: a block is 2 k rows of 512 bytes; lane l writes physical column l % 32 of
+  //     k row 2 b + l / 32 and so fetches logical column (l % 32) ^ (4 (k % 4)).
+  // Offsets are tile-relative on workgroup-uniform bases; rows beyond the valid range
+  // are clamped as Operand describes.
   constexpr int kBlocksPerWave = (kTileV + kTileT) / 8 / (kThreads / 64);  // 8
   constexpr int kWBlocks = kTileV / 8;
-  int src_off[kBlocksPerWave];
+  int64_t src_off[kBlocksPerWave];  // K-contiguous: offset at k = 0
+  int kmaj_row[kBlocksPerWave];     // K-major: k row within the step
 #pragma unroll
   for (int i = 0; i < kBlocksPerWave; ++i) {
     const int blk = i * 8 + wave;
-    const bool is_w = i < kWBlocks / 8;
-    const int bb = is_w ? blk : blk - kWBlocks;
-    const int row = bb * 8 + (lane >> 3);
-    const int col = ((lane & 7) ^ ((row >> 1) & 7)) * 8;
-    src_off[i] = is_w ? (min(row, w_last) * (int)ldw + col) : (min(row, h_last) * (int)ldh + col);
+    const bool is_a = i < kWBlocks / 8;
+    const int bb = is_a ? blk : blk - kWBlocks;
+    const bool kmaj = is_a ? A_KMAJOR : B_KMAJOR;
+    const Operand& op = is_a ? A : B;
+    if (!kmaj) {
+      const int row = bb * 8 + (lane >> 3);
+      const int col = ((lane & 7) ^ ((row >> 1) & 7)) * 8;
+      src_off[i] = (int64_t)min(row, op.last) * op.ld + col;
+      kmaj_row[i] = 0;
+    } else {
+      const int k = bb * 2 + (lane >> 5);
+      const int col = min(((lane & 31) ^ ((k & 3) << 2)) * 8, op.last & ~7);
+      src_off[i] = col;
+      kmaj_row[i] = k;
+    }
   }
-  auto issue_stage = [&](int64_t k0, int stage) {
+  auto issue_stage = [&](int64_t k, int stage) {
 #pragma unroll
     for (int i = 0; i < kBlocksPerWave; ++i) {
       const int blk = i * 8 + wave;
-      const bool is_w = i < kWBlocks / 8;
-      const uint16_t* src = (is_w ? Wt : Ht) + k0 + src_off[i];
+      const bool is_a = i < kWBlocks / 8;
+      const bool kmaj = is_a ? A_KMAJOR : B_KMAJOR;
+      const Operand& op = is_a ? A : B;
+      const uint16_t* src;
+      if (!kmaj)
+        src = op.p + k + src_off[i];
+      else
+        src = op.p + min(k + kmaj_row[i], op.k_last) * op.ld + src_off[i];
       char* dst = smem + stage * kStageBytes + blk * 1024;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
   };
+  // LDS reads per MFMA step: four A fragments and two B fragments, two transpose loads
+  // each on a K-major side.
+  constexpr int kReads = (A_KMAJOR ? 8 : 4) + (B_KMAJOR ? 4 : 2);
 
-  const int frow = lane & 31;
-  const int fhalf = lane >> 5;
-  issue_stage(0, 0);
+  issue_stage(k0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     // Stage kt has landed for every wave, and every wave is done reading stage kt - 1,
     // whose buffer the loads of stage kt + 1 now overwrite.  A wave waits at normal issue
@@ -128,23 +211,18 @@ __device__ __forceinline__ void mma_tile(const uint16_t* __restrict__ At, int64_
     // Fragments of step ks + 1 are read from LDS while the MFMAs of step ks run.
     bf16x8 af[2][4], bfr[2][2];
     auto read_frags = [&](int ks, int buf) {
-      const int c16 = 2 * ks + fhalf;
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        af[buf][a] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const U4*>(wb + lds_offset(wv * 128 + a * 32 + frow, c16)));
+      for (int a = 0; a < 4; ++a) af[buf][a] = read_fragment<A_KMAJOR>(wb, wv * 128 + a * 32, ks);
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        bfr[buf][b] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const U4*>(hb + lds_offset(wt * 64 + b * 32 + frow, c16)));
+      for (int b = 0; b < 2; ++b) bfr[buf][b] = read_fragment<B_KMAJOR>(hb, wt * 64 + b * 32, ks);
     };
     read_frags(0, 0);
     __builtin_amdgcn_s_setprio(1);
-    sched_group(kSchedDsRead, 6);
+    sched_group(kSchedDsRead, kReads);
     // Loads of stage kt + 1 into the other buffer.  Issued on every stage (the last one
     // repeats stage nk - 1 into the idle buffer) so that they stay in this scheduling
     // region and can be spread between the MFMAs of step 0 instead of stalling the wave.
-    issue_stage((int64_t)min(kt + 1, nk - 1) * kBK, (kt + 1) & 1);
+    issue_stage(k0 + (int64_t)min(kt + 1, nk - 1) * kBK, (kt + 1) & 1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       if (ks + 1 < 4) read_frags(ks + 1, (ks + 1) & 1);
@@ -155,23 +233,19 @@ __device__ __forceinline__ void mma_tile(const uint16_t* __restrict__ At, int64_
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][a], bfr[ks & 1][b],
                                                               acc[a][b], 0, 0, 0);
       // Instruction order: step 0 interleaves its eight MFMAs with the eight loads of the
-      // next stage, then reads the fragments of step 1; steps 1 and 2 interleave the six
-      // LDS reads of the following step with their first six MFMAs.  Left to itself the
-      // scheduler merges the two fragment buffers, waits on each read right away and
-      // issues all stage loads in one burst ahead of the MFMAs.
+      // next stage, then reads the fragments of step 1; steps 1 and 2 spread the LDS reads
+      // of the following step over their MFMAs.  Left to itself the scheduler merges the
+      // two fragment buffers, waits on each read right away and issues all stage loads in
+      // one burst ahead of the MFMAs.
       if (ks == 0) {
 #pragma unroll
         for (int q = 0; q < kBlocksPerWave; ++q) {
           sched_group(kSchedMfma, 1);
           sched_group(kSchedVmemRead, 1);
         }
-        sched_group(kSchedDsRead, 6);
+        sched_group(kSchedDsRead, kReads);
       } else if (ks + 1 < 4) {
-#pragma unroll
-        for (int q = 0; q < 6; ++q) {
-          sched_group(kSchedMfma, 1);
-          sched_group(kSchedDsRead, 1);
-        }
+        sched_reads_over_mfmas<kReads, 0>();
         sched_group(kSchedMfma, 2);
       } else {
         sched_group(kSchedMfma, 8);
@@ -180,6 +254,18 @@ __device__ __forceinline__ void mma_tile(const uint16_t* __restrict__ At, int64_
   }
   __builtin_amdgcn_s_setprio(0);
   wait_dma();  // the repeated last-stage loads land before the caller reuses the LDS
+}
+
+// Both operands K-contiguous.
+//   At, Bt       first row of the tile's A / B rows (element 0 of K)
+//   lda, ldb     row strides (elements)
+//   a_last, b_last  last valid row index within the tile
+__device__ __forceinline__ void mma_tile(const uint16_t* __restrict__ At, int64_t lda,
+                                         int a_last, const uint16_t* __restrict__ Bt,
+                                         int64_t ldb, int b_last, int64_t k0, int nk, char* smem,
+                                         floatx16 (&acc)[4][2]) {
+  mma_tile_op<false, false>(Operand{At, lda, a_last, 0}, Operand{Bt, ldb, b_last, 0}, k0, nk,
+                            smem, acc);
 }
 
 }  // namespace mma

@@ -194,8 +194,11 @@ def test_linear_backward_workspace_and_validation(L):
     T, V, d = 2048, 151936, 4096
     ws = L.workspace_bytes(B.OP_LINEAR_BACKWARD, T, V, d, 1)
     Vp, Tp = 151936, 2048
-    assert ws >= L.workspace_bytes(B.OP_LINEAR, T, V, d, 1) + d * Vp * 2 + d * Tp * 2 + \
-        2 * T * Vp * 2 + 8 * T * d * 4
+    fwd = L.workspace_bytes(B.OP_LINEAR, T, V, d, 1)
+    # forward workspace, row states and constants, H^T, dX and dX^T in bf16, 8 dH partials;
+    # W is read in place (no transposed copy)
+    need = fwd + d * Tp * 2 + T * Vp * 2 + V * Tp * 2 + 8 * T * d * 4
+    assert need <= ws <= need + (1 << 20)
     assert L.workspace_bytes(B.OP_LINEAR_BACKWARD, 0, V, d, 1) == 0
     with pytest.raises(B.RlkError):
         L.workspace_bytes(B.OP_LINEAR_BACKWARD, T, V, 100, 1)         # d not a multiple of 64
