@@ -165,3 +165,24 @@ def test_saved_row_states_give_the_same_bits(lib):
         dh, dw = lib.linear_logprob_backward(hd, wd, td, 0.7, 1, gld, ged, row_states=states)
         assert torch.equal(dh.view(torch.int32), dh0.view(torch.int32)), split
         assert torch.equal(dw.view(torch.int32), dw0.view(torch.int32)), split
+
+
+def test_strided_operands_give_the_same_bits(lib):
+    """Hidden states and LM head given as column slices of wider tensors (row strides above
+    d; W is read in place by the dH contraction) give the contiguous inputs' bits."""
+    import torch
+    T, d, V = 100, 192, 3001
+    case = S.random_fused_case(T, d, V, seed=106, w_sigma=3.0 / math.sqrt(d))
+    gl, ge = weights(T, 107)
+    hd, wd, td = bits_dev(case.h_bits), bits_dev(case.w_bits), dev(case.targets)
+    gld, ged = dev(gl), dev(ge)
+    announce("linear backward strided hidden and weight")
+    dh0, dw0 = lib.linear_logprob_backward(hd, wd, td, 1.0, 1, gld, ged)
+    h_big = torch.zeros((T, d + 64), dtype=torch.int16, device="cuda")
+    w_big = torch.zeros((V, d + 72), dtype=torch.int16, device="cuda")
+    h_big[:, 8:8 + d] = hd
+    w_big[:, 16:16 + d] = wd
+    dh, dw = lib.linear_logprob_backward(h_big[:, 8:8 + d], w_big[:, 16:16 + d], td, 1.0, 1, gld,
+                                         ged)
+    assert torch.equal(dh.view(torch.int32), dh0.view(torch.int32))
+    assert torch.equal(dw.view(torch.int32), dw0.view(torch.int32))
