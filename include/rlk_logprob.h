@@ -30,7 +30,8 @@
  *   - every call is asynchronous on `stream` (a hipStream_t passed as void*, NULL =
  *     the default stream); it never allocates, never synchronizes and never reads
  *     device memory on the host; results are valid once the stream has reached the
- *     point of the call;
+ *     point of the call; a call only launches kernels (workspace clearing included),
+ *     so it can be captured into a HIP graph and replayed;
  *   - arguments are validated on the host before anything is launched; on error
  *     nothing is launched and no output is written;
  *   - n_tokens == 0 returns RLK_OK and launches nothing;
