@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace rlk {
 namespace mma {
 
@@ -197,8 +199,23 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
   // each on a K-major side.
   constexpr int kReads = (A_KMAJOR ? 8 : 4) + (B_KMAJOR ? 4 : 2);
 
-  issue_stage(k0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
+  // Fragments of MFMA step ks live in buffer ks % 2; the fragments of step ks + 1 are read
+  // from LDS while the MFMAs of step ks run.
+  bf16x8 af[2][4], bfr[2][2];
+  auto mfma_step = [&](int buf) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][a], bfr[buf][b], acc[a][b],
+                                                            0, 0, 0);
+  };
+  // One K step.  The last MFMA step of K step kt - 1 (DEFERRED) is held back until after
+  // the barrier that opens K step kt: its fragments are already in registers, so its
+  // eight MFMAs keep the matrix unit busy while the first fragments of K step kt come
+  // from LDS, instead of both waves of the SIMD idling through that latency.  Every
+  // accumulator still sees its MFMAs in K order.
+  auto k_step = [&](int kt, auto deferred) {
     // Stage kt has landed for every wave, and every wave is done reading stage kt - 1,
     // whose buffer the loads of stage kt + 1 now overwrite.  A wave waits at normal issue
     // priority and runs its MFMA steps at raised priority, so that the SIMD's arbiter
@@ -208,8 +225,6 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
     lds_barrier();
     const char* wb = smem + (kt & 1) * kStageBytes;
     const char* hb = wb + kTileV * kBK * 2;
-    // Fragments of step ks + 1 are read from LDS while the MFMAs of step ks run.
-    bf16x8 af[2][4], bfr[2][2];
     auto read_frags = [&](int ks, int buf) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) af[buf][a] = read_fragment<A_KMAJOR>(wb, wv * 128 + a * 32, ks);
@@ -221,37 +236,35 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
     sched_group(kSchedDsRead, kReads);
     // Loads of stage kt + 1 into the other buffer.  Issued on every stage (the last one
     // repeats stage nk - 1 into the idle buffer) so that they stay in this scheduling
-    // region and can be spread between the MFMAs of step 0 instead of stalling the wave.
+    // region and can be spread between MFMAs instead of stalling the wave.
     issue_stage(k0 + (int64_t)min(kt + 1, nk - 1) * kBK, (kt + 1) & 1);
+    // Instruction order (left to itself the scheduler merges the two fragment buffers,
+    // waits on each read right away and issues all stage loads in one burst ahead of the
+    // MFMAs): the deferred MFMAs interleaved with the eight stage loads; then MFMA steps
+    // 0..2, each spreading the LDS reads of the following step over its MFMAs.
+    if constexpr (decltype(deferred)::value) {
+      mfma_step(1);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks + 1 < 4) read_frags(ks + 1, (ks + 1) & 1);
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][a], bfr[ks & 1][b],
-                                                              acc[a][b], 0, 0, 0);
-      // Instruction order: step 0 interleaves its eight MFMAs with the eight loads of the
-      // next stage, then reads the fragments of step 1; steps 1 and 2 spread the LDS reads
-      // of the following step over their MFMAs.  Left to itself the scheduler merges the
-      // two fragment buffers, waits on each read right away and issues all stage loads in
-      // one burst ahead of the MFMAs.
-      if (ks == 0) {
-#pragma unroll
-        for (int q = 0; q < kBlocksPerWave; ++q) {
-          sched_group(kSchedMfma, 1);
-          sched_group(kSchedVmemRead, 1);
-        }
-        sched_group(kSchedDsRead, kReads);
-      } else if (ks + 1 < 4) {
-        sched_reads_over_mfmas<kReads, 0>();
-        sched_group(kSchedMfma, 2);
-      } else {
-        sched_group(kSchedMfma, 8);
+      for (int q = 0; q < kBlocksPerWave; ++q) {
+        sched_group(kSchedMfma, 1);
+        sched_group(kSchedVmemRead, 1);
       }
+    } else {
+      sched_group(kSchedVmemRead, kBlocksPerWave);
     }
-  }
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {
+      read_frags(ks + 1, (ks + 1) & 1);
+      mfma_step(ks & 1);
+      sched_reads_over_mfmas<kReads, 0>();
+      sched_group(kSchedMfma, 2);
+    }
+  };
+
+  issue_stage(k0, 0);
+  k_step(0, std::false_type{});
+  for (int kt = 1; kt < nk; ++kt) k_step(kt, std::true_type{});
+  mfma_step(1);  // the last K step's deferred MFMA step
   __builtin_amdgcn_s_setprio(0);
   wait_dma();  // the repeated last-stage loads land before the caller reuses the LDS
 }
