@@ -20,8 +20,8 @@
 // x 4 (token), each wave 128 x 64 = 4 x 2 MFMA blocks.  K step 64 with two LDS stages
 // (64 KiB each: the W and H slices with an XOR swizzle on 16-byte columns so that
 // ds_read_b128 of 16 consecutive rows hits distinct banks).  Workgroup ids are remapped
-// so that the token tiles of one vocabulary tile run back to back on the same XCD and
-// share its W slice in that XCD's L2.
+// so that each XCD runs a few vocabulary tiles times a group of 8 token tiles at once,
+// sharing their W and H slices in that XCD's L2.
 
 #include <hip/hip_runtime.h>
 
@@ -98,15 +98,9 @@ __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
     WireState* __restrict__ tile_states, float* __restrict__ target_logit) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
 
-  // Remap the hardware id (dispatched round-robin over the 8 XCDs) so that logically
-  // consecutive tiles -- the token tiles of one vocabulary tile -- share an XCD.
-  const int64_t nb = g.n_vt * g.n_tt;
-  const int64_t per_xcd = (nb + 7) / 8;
-  const int64_t hw = blockIdx.x;
-  const int64_t logical = (hw % 8) * per_xcd + hw / 8;
-  if (logical >= nb) return;
-  const int64_t vt = logical / g.n_tt;
-  const int64_t tt = logical % g.n_tt;
+  // Vocabulary tiles x token tiles, token tiles in groups of 8 (see grouped_tile_of).
+  int64_t vt, tt;
+  if (!mma::grouped_tile_of<8>(g.n_vt, g.n_tt, vt, tt)) return;
   const int64_t chunk = vt / g.tpc;
   const int64_t kin = vt % g.tpc;
   const int64_t chunk_lo = min(chunk * g.Vc, g.V);

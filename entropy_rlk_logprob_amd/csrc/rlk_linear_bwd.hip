@@ -96,17 +96,10 @@ __device__ __forceinline__ float logit_grad(float x, bool is_target, const GradR
   return r.beta * (r.gl * ((is_target ? 1.0f : 0.0f) - p) - r.ge * ent);
 }
 
-// Output tile id -> (row tile, column tile), remapped so that consecutive logical tiles
-// (the column tiles of one row tile) run on the same XCD and share its row slice in L2.
+// Output tile id -> (row tile, column tile): column tiles in groups of 8, row-tile-major
+// within a group (see grouped_tile_of).
 __device__ __forceinline__ bool tile_of(int64_t n_rt, int64_t n_ct, int64_t& rt, int64_t& ct) {
-  const int64_t nb = n_rt * n_ct;
-  const int64_t per_xcd = (nb + 7) / 8;
-  const int64_t hw = blockIdx.x;
-  const int64_t logical = (hw % 8) * per_xcd + hw / 8;
-  if (logical >= nb) return false;
-  rt = logical / n_ct;
-  ct = logical % n_ct;
-  return true;
+  return mma::grouped_tile_of<8>(n_rt, n_ct, rt, ct);
 }
 
 // Step 3: logits tile (vocab rows x tokens), then its gradient in bf16.
@@ -240,9 +233,9 @@ __global__ __launch_bounds__(256) void zero_cols_kernel(uint16_t* __restrict__ p
 // clamped, the other operand holding zeros there).  Stored row-major at C[m * ldc + n]
 // (32 lanes write 128 contiguous bytes of a row).  Split s (blockIdx.y) covers K steps
 // [s * steps, (s + 1) * steps) and writes C + s * split_stride; an empty range writes 0.
-// SHARE_B: tiles are taken column-tile-major (consecutive logical tiles share a B slice),
-// else row-tile-major (they share an A slice): the larger operand is fetched from HBM once
-// and shared in an XCD's L2.
+// Tile order (tile_of): SHARE_B groups row tiles and runs column-tile-major within a group
+// (consecutive logical tiles share a B slice), else the reverse (they share an A slice):
+// the larger operand is fetched from HBM once and shared in an XCD's L2.
 template <bool A_KMAJOR, bool B_KMAJOR, bool SHARE_B>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const uint16_t* __restrict__ A, int64_t lda, int64_t M, int64_t a_klast,
@@ -397,8 +390,8 @@ hipError_t launch_linear_backward(const LinearArgs& fwd, const float* g_lp, cons
   }
   if (dW) {
     // dW[v, k] = sum_t dX^T[v, t] H^T[k, t]: A = dX^T (M = V), B = H^T (N = d; a transposed
-    // copy of H, small), both K-contiguous, K = Tp; row-tile-major so that the tiles
-    // sharing a dX^T slice run together; stored row-major (32 lanes write 128 contiguous
+    // copy of H, small), both K-contiguous, K = Tp; row-tile-major within groups of 8
+    // column tiles, so that the tiles sharing a dX^T slice run together; stored row-major (32 lanes write 128 contiguous
     // bytes of a dW row).  (Reading dX in place as a K-major A operand measured 0.6 ms
     // slower at T = 2048, d = 4096, V = 151936 than writing dX^T in step 3.)
     uint16_t* ht = reinterpret_cast<uint16_t*>(base + L.ht);

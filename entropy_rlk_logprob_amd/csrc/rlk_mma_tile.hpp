@@ -269,6 +269,28 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
   wait_dma();  // the repeated last-stage loads land before the caller reuses the LDS
 }
 
+// Workgroup id -> (row tile, column tile) of an n_rt x n_ct grid of output tiles.  The
+// hardware hands workgroup ids out round-robin over the 8 XCDs; the remap gives each XCD a
+// contiguous range of logical tiles.  Logical tiles run one group of up to G column tiles
+// at a time, row-tile-major within the group, so that the ~32 tiles an XCD runs at once
+// are a few row tiles times one column group and share both operands' slices in that
+// XCD's L2.  Returns false for the padding ids beyond the grid.
+template <int G>
+__device__ __forceinline__ bool grouped_tile_of(int64_t n_rt, int64_t n_ct, int64_t& rt,
+                                                int64_t& ct) {
+  const int64_t nb = n_rt * n_ct;
+  const int64_t per_xcd = (nb + 7) / 8;
+  const int64_t hw = blockIdx.x;
+  const int64_t logical = (hw % 8) * per_xcd + hw / 8;
+  if (logical >= nb) return false;
+  const int64_t grp = logical / (G * n_rt);
+  const int64_t gsz = min((int64_t)G, n_ct - grp * G);
+  const int64_t idx = logical - grp * G * n_rt;
+  rt = idx / gsz;
+  ct = grp * G + idx % gsz;
+  return true;
+}
+
 // Both operands K-contiguous.
 //   At, Bt       first row of the tile's A / B rows (element 0 of K)
 //   lda, ldb     row strides (elements)
