@@ -50,6 +50,25 @@ def test_shapes_vs_oracle_and_split_bitwise(lib, T, d, V, tau):
             assert bitwise_equal(lp, ref[0]) and bitwise_equal(ent, ref[1]), split
 
 
+def test_token_tile_groups_with_partial_last_group(lib):
+    """T = 2600: 11 token tiles, which the kernel runs as a group of 8 and a partial group
+    of 3.  Every row against the oracle; the rows of the partial group alone, and vocab
+    split 4, give the same bits."""
+    T, d, V = 2600, 64, 3000
+    announce(f"linear T={T} d={d} V={V} (token tile groups 8 + 3)")
+    case = S.random_fused_case(T, d, V, seed=9100, h_sigma=1.0, w_sigma=3.0 / math.sqrt(d))
+    olp, oent = oracle.linear_logprob_entropy(f32(case.h_bits), f32(case.w_bits), case.targets,
+                                              1.0)
+    h, w, t = bits_dev(case.h_bits), bits_dev(case.w_bits), dev(case.targets)
+    lp, ent = run_linear(lib, h, w, t)
+    assert max_abs(lp, olp) <= TOL_LINEAR and max_abs(ent, oent) <= TOL_LINEAR
+    lp4, ent4 = run_linear(lib, h, w, t, 1.0, 4)
+    assert bitwise_equal(lp4, lp) and bitwise_equal(ent4, ent)
+    lo = 8 * 256
+    lpt, entt = run_linear(lib, h[lo:], w, t[lo:])
+    assert bitwise_equal(lpt, lp[lo:]) and bitwise_equal(entt, ent[lo:])
+
+
 def test_uniform_when_weight_is_zero(lib):
     announce("linear zero weight -> uniform")
     T, d, V = 5, 128, 3000

@@ -84,6 +84,27 @@ def test_shapes_vs_oracle_and_split_bitwise(lib, T, d, V, tau):
     assert bitwise_equal(dh_only, first[0]) and bitwise_equal(dw_only, first[1])
 
 
+def test_tile_groups_with_partial_last_group(lib):
+    """T = 2600 (11 token tiles) and d = 2304 (9 hidden tiles): the tile grids of the
+    logit-gradient kernel and of both GEMMs run a full group of 8 column tiles and a
+    partial one.  dH and dW against the oracle; dH rows of the partial token group alone
+    give the same bits."""
+    T, d, V = 2600, 2304, 1000
+    announce(f"linear backward T={T} d={d} V={V} (tile groups 8 + 3 and 8 + 1)")
+    case = S.random_fused_case(T, d, V, seed=9600, h_sigma=1.0, w_sigma=3.0 / math.sqrt(d))
+    gl, ge = weights(T, 9601)
+    h, w = f32(case.h_bits), f32(case.w_bits)
+    gx = oracle.logits_grad(h @ w.T, case.targets, 1.0, gl, ge)
+    hd, wd, td = bits_dev(case.h_bits), bits_dev(case.w_bits), dev(case.targets)
+    gld, ged = dev(gl), dev(ge)
+    dh, dw = run_bwd(lib, hd, wd, td, 1.0, 1, gld, ged)
+    check(dh, gx @ w, bound(gx, w, -(-V // 64) * 64))
+    check(dw, gx.T @ h, bound(gx.T, h, -(-T // 64) * 64))
+    lo = 8 * 256
+    part, _ = run_bwd(lib, hd[lo:], wd, td[lo:], 1.0, 1, gld[lo:], ged[lo:], True, False)
+    assert bitwise_equal(part, dh[lo:])
+
+
 def test_entropy_only_and_masked_rows(lib):
     T, d, V = 70, 128, 3001
     case = S.random_fused_case(T, d, V, seed=96, w_sigma=0.25)
