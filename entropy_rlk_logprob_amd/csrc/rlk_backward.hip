@@ -49,8 +49,9 @@ template <bool VEC>
 __global__ __launch_bounds__(kGradThreads) void logits_grad_kernel(
     const float* X, int64_t ld, int64_t V, const int64_t* __restrict__ targets,
     float c, double beta, const float* __restrict__ g_lp, const float* __restrict__ g_ent,
-    const WireState* __restrict__ root, float* G, int64_t ldg) {
-  const int64_t row = blockIdx.x;
+    const WireState* __restrict__ root, float* G, int64_t ldg, int64_t T) {
+  const int64_t row = linear_block();
+  if (row >= T) return;
   __shared__ GradRow rc;
   if (threadIdx.x == 0) {
     GradRow r;
@@ -121,13 +122,13 @@ hipError_t launch_logits_backward(const LogitsArgs& a, const float* g_lp, const 
     if (e != hipSuccess) return e;
   }
   const int64_t spans = (a.V + kGradColsPerBlock - 1) / kGradColsPerBlock;
-  const dim3 grid((unsigned)a.T, (unsigned)(spans < 4096 ? spans : 4096));
+  const dim3 grid = split_grid(a.T, (unsigned)(spans < 4096 ? spans : 4096));
   if (vec)
     hipLaunchKernelGGL((logits_grad_kernel<true>), grid, dim3(kGradThreads), 0, stream, a.X, a.ld,
-                       a.V, a.targets, a.c, a.beta, g_lp, g_ent, a.root, G, ldg);
+                       a.V, a.targets, a.c, a.beta, g_lp, g_ent, a.root, G, ldg, a.T);
   else
     hipLaunchKernelGGL((logits_grad_kernel<false>), grid, dim3(kGradThreads), 0, stream, a.X,
-                       a.ld, a.V, a.targets, a.c, a.beta, g_lp, g_ent, a.root, G, ldg);
+                       a.ld, a.V, a.targets, a.c, a.beta, g_lp, g_ent, a.root, G, ldg, a.T);
   return hipGetLastError();
 }
 

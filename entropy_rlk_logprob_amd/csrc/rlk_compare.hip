@@ -104,7 +104,9 @@ __device__ __forceinline__ void add_token(Partial& p, float a, float b) {
 __global__ __launch_bounds__(kCmpThreads) void compare_blocks_kernel(
     const float* __restrict__ train, const float* __restrict__ rollout,
     const uint8_t* __restrict__ mask, int64_t T, Partial* __restrict__ partials) {
-  const int64_t base = (int64_t)blockIdx.x * kCmpTokensPerBlock + threadIdx.x;
+  const int64_t blk = linear_block();
+  if (blk * kCmpTokensPerBlock >= T) return;
+  const int64_t base = blk * kCmpTokensPerBlock + threadIdx.x;
   Partial p = zero_partial();
 #pragma unroll
   for (int k = 0; k < kCmpPerThread; ++k) {
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(kCmpThreads) void compare_blocks_kernel(
     if (i < T && (!mask || mask[i] != 0)) add_token(p, train[i], rollout[i]);
   }
   const Partial r = block_combine(p);
-  if (threadIdx.x == 0) partials[blockIdx.x] = r;
+  if (threadIdx.x == 0) partials[blk] = r;
 }
 
 __global__ __launch_bounds__(kCmpThreads) void compare_final_kernel(
@@ -149,7 +151,7 @@ hipError_t launch_compare(const float* train, const float* rollout, const uint8_
   const int64_t nb = compare_blocks(T);
   Partial* partials = static_cast<Partial*>(ws);
   if (nb > 0) {
-    hipLaunchKernelGGL(compare_blocks_kernel, dim3((unsigned)nb), dim3(kCmpThreads), 0, stream,
+    hipLaunchKernelGGL(compare_blocks_kernel, split_grid(nb), dim3(kCmpThreads), 0, stream,
                        train, rollout, mask, T, partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

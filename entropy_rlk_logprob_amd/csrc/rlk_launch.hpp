@@ -10,6 +10,24 @@ namespace rlk {
 
 struct WireState;
 
+// Launch grids.  A dispatch holds at most 2^32 - 1 work-items along each dimension, so a
+// grid of n blocks is laid out as x = min(n, kGridX) blocks times z = ceil(n / x): the
+// kernel's block index is blockIdx.z * gridDim.x + blockIdx.x (linear_block), and the
+// blocks at or beyond n return at once.  kGridX = 2^22 keeps blocks of up to 512 threads
+// at 2^31 work-items along x, and is a multiple of 8, so that a block's XCD (its index in
+// dispatch order mod 8) stays blockIdx.x mod 8.
+constexpr int64_t kGridX = int64_t(1) << 22;
+
+inline dim3 split_grid(int64_t n, unsigned y = 1) {
+  if (n < 1) n = 1;
+  const int64_t x = n < kGridX ? n : kGridX;
+  return dim3((unsigned)x, y, (unsigned)((n + x - 1) / x));
+}
+
+__device__ __forceinline__ int64_t linear_block() {
+  return (int64_t)blockIdx.z * gridDim.x + blockIdx.x;
+}
+
 // Canonical vocabulary partition shared by both paths: 8 chunks of Vc columns,
 // Vc = 4 * ceil(ceil(V / 8) / 4).
 inline int64_t chunk_cols(int64_t V) {

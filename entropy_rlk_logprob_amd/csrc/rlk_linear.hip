@@ -233,7 +233,7 @@ __global__ __launch_bounds__(64 * CPS) void tile_tree_kernel(
   const int ci = threadIdx.x >> 6;
   const int tl8 = lane & 7;
   const int blk = lane >> 3;
-  const int64_t tok = (int64_t)blockIdx.x * 8 + tl8;
+  const int64_t tok = linear_block() * 8 + tl8;
   const int shard = blockIdx.y;
   const int64_t chunk = (int64_t)shard * CPS + ci;
   __shared__ State cs[CPS][8];
@@ -317,7 +317,7 @@ hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream) {
   char* base = static_cast<char*>(a.ws);
   const int64_t nb = g.n_vt * g.n_tt;
   const int64_t nb_pad = ((nb + 7) / 8) * 8;
-  hipLaunchKernelGGL(linear_tile_kernel, dim3((unsigned)nb_pad), dim3(kThreads), 0, stream, a.H,
+  hipLaunchKernelGGL(linear_tile_kernel, split_grid(nb_pad), dim3(kThreads), 0, stream, a.H,
                      a.ldh, a.W, a.ldw, a.d, g, a.targets, a.c,
                      reinterpret_cast<WireState*>(base + L.tile_states),
                      reinterpret_cast<float*>(base + L.target_logit));
@@ -327,7 +327,7 @@ hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream) {
   const WireState* tiles = reinterpret_cast<const WireState*>(base + L.tile_states);
   const float* tl = reinterpret_cast<const float*>(base + L.target_logit);
   WireState* sws = reinterpret_cast<WireState*>(base + L.shard_states);
-  const dim3 tgrid((unsigned)((a.T + 7) / 8), (unsigned)a.S);
+  const dim3 tgrid = split_grid((a.T + 7) / 8, (unsigned)a.S);
   switch (a.S) {
     case 1:
       hipLaunchKernelGGL((tile_tree_kernel<8>), tgrid, dim3(512), 0, stream, tiles, tl, g,

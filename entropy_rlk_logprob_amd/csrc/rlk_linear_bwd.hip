@@ -171,8 +171,9 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(
     const uint16_t* __restrict__ in, int64_t ldin, int64_t R, int64_t C,
     uint16_t* __restrict__ out, int64_t ldout, int64_t Rp) {
   __shared__ uint16_t tile[64][64 + 8];
-  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int64_t r0 = linear_block() * 64;
   const int64_t c0 = (int64_t)blockIdx.y * 64;
+  if (r0 >= Rp) return;
   const int tid = threadIdx.x;
   // load: thread -> rows tid / 8 and tid / 8 + 32, columns 8 (tid % 8) .. + 8
   const bool vec_in = (ldin % 8 == 0) && (c0 + 64 <= C);
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                             int64_t stride, int64_t T, int64_t d,
                                                             float* __restrict__ out, int64_t ldo) {
-  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // quad index
+  const int64_t q = linear_block() * 256 + threadIdx.x;  // quad index
   const int64_t nq = T * (d / 4);
   if (q >= nq) return;
   const int64_t t = q / (d / 4), k = 4 * (q % (d / 4));
@@ -367,7 +368,7 @@ hipError_t launch_linear_backward(const LinearArgs& fwd, const float* g_lp, cons
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   const int64_t tiles_x = ((V + kTile - 1) / kTile) * ((T + kTile - 1) / kTile);
-  hipLaunchKernelGGL(dx_tile_kernel, dim3((unsigned)((tiles_x + 7) / 8 * 8)), dim3(kThreads), 0,
+  hipLaunchKernelGGL(dx_tile_kernel, split_grid((tiles_x + 7) / 8 * 8), dim3(kThreads), 0,
                      stream, a.H, a.ldh, a.W, a.ldw, d, T, V, a.c, rc, dx, L.Vp, dxt, L.Tp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
@@ -379,12 +380,12 @@ hipError_t launch_linear_backward(const LinearArgs& fwd, const float* g_lp, cons
     const int64_t steps = (L.Vp / kBK + kDhSplits - 1) / kDhSplits;
     const int64_t tiles = ((T + kTile - 1) / kTile) * ((d + kTile - 1) / kTile);
     hipLaunchKernelGGL((gemm_kernel<false, true, true>),
-                       dim3((unsigned)((tiles + 7) / 8 * 8), kDhSplits), dim3(kThreads), 0,
+                       split_grid((tiles + 7) / 8 * 8, kDhSplits), dim3(kThreads), 0,
                        stream, dx, L.Vp, T, (int64_t)0, a.W, a.ldw, d, V - 1, L.Vp, steps, part,
                        d, T * d);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t nq = T * (d / 4);
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0,
+    hipLaunchKernelGGL(splitk_reduce_kernel, split_grid((nq + 255) / 256), dim3(256), 0,
                        stream, part, T * d, T, d, dH, ld_dh);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -395,12 +396,12 @@ hipError_t launch_linear_backward(const LinearArgs& fwd, const float* g_lp, cons
     // bytes of a dW row).  (Reading dX in place as a K-major A operand measured 0.6 ms
     // slower at T = 2048, d = 4096, V = 151936 than writing dX^T in step 3.)
     uint16_t* ht = reinterpret_cast<uint16_t*>(base + L.ht);
-    hipLaunchKernelGGL(transpose_pad_kernel, dim3((unsigned)(L.Tp / 64), (unsigned)(d / 64)),
+    hipLaunchKernelGGL(transpose_pad_kernel, split_grid(L.Tp / 64, (unsigned)(d / 64)),
                        dim3(256), 0, stream, a.H, a.ldh, T, d, ht, L.Tp, L.Tp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t tiles = ((V + kTile - 1) / kTile) * ((d + kTile - 1) / kTile);
     hipLaunchKernelGGL((gemm_kernel<false, false, false>),
-                       dim3((unsigned)((tiles + 7) / 8 * 8), 1), dim3(kThreads), 0, stream, dxt,
+                       split_grid((tiles + 7) / 8 * 8), dim3(kThreads), 0, stream, dxt,
                        L.Tp, V, (int64_t)0, ht, L.Tp, d, (int64_t)0, L.Tp, L.Tp / kBK, dW, ld_dw,
                        (int64_t)0);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -241,7 +241,8 @@ void row_reduce_kernel(
     float* __restrict__ ent_out, WireState* __restrict__ ws, WireState* __restrict__ root) {
   constexpr int WAVES = waves_for<E>(CPS);
   constexpr int CPW = chunks_per_wave<E>(CPS);
-  const int64_t row = blockIdx.x;
+  const int64_t row = linear_block();
+  if (row >= T) return;
   const int shard = blockIdx.y;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -374,7 +375,7 @@ __global__ __launch_bounds__(256) void shard_merge_kernel(
 
 template <typename E, int CPS>
 hipError_t launch_rows_t(const E* X, const LogitsArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.T, (unsigned)(8 / CPS));
+  const dim3 grid = split_grid(a.T, (unsigned)(8 / CPS));
   const dim3 block(64 * waves_for<E>(CPS));
   if (a.vec)
     hipLaunchKernelGGL((row_reduce_kernel<E, CPS, true>), grid, block, 0, stream, X, a.ld, a.T,

@@ -27,6 +27,8 @@
 
 #include <type_traits>
 
+#include "rlk_launch.hpp"
+
 namespace rlk {
 namespace mma {
 
@@ -269,9 +271,9 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
   wait_dma();  // the repeated last-stage loads land before the caller reuses the LDS
 }
 
-// Workgroup id -> (row tile, column tile) of an n_rt x n_ct grid of output tiles.  The
-// hardware hands workgroup ids out round-robin over the 8 XCDs; the remap gives each XCD a
-// contiguous range of logical tiles.  Logical tiles run one group of up to G column tiles
+// Workgroup id -> (row tile, column tile) of an n_rt x n_ct grid of output tiles, launched
+// as split_grid(8 ceil(n_rt n_ct / 8)).  The hardware hands workgroup ids out round-robin
+// over the 8 XCDs; the remap gives each XCD a contiguous range of logical tiles.  Logical tiles run one group of up to G column tiles
 // at a time, row-tile-major within the group, so that the ~32 tiles an XCD runs at once
 // are a few row tiles times one column group and share both operands' slices in that
 // XCD's L2.  Returns false for the padding ids beyond the grid.
@@ -280,7 +282,8 @@ __device__ __forceinline__ bool grouped_tile_of(int64_t n_rt, int64_t n_ct, int6
                                                 int64_t& ct) {
   const int64_t nb = n_rt * n_ct;
   const int64_t per_xcd = (nb + 7) / 8;
-  const int64_t hw = blockIdx.x;
+  const int64_t hw = linear_block();
+  if (hw >= 8 * per_xcd) return false;
   const int64_t logical = (hw % 8) * per_xcd + hw / 8;
   if (logical >= nb) return false;
   const int64_t grp = logical / (G * n_rt);
