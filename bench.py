@@ -24,6 +24,10 @@ Also reported on the same JSON line:
                 algorithmic bytes (one read of the logits, one write of the gradient);
   fused_backward  rlk_linear_logprob_backward on the Qwen3-8B shape: ms per call and
                 TFLOP/s over 3 x 2 T V d flops (logits, dH, dW) vs the bf16 peak.
+  ceilings      what the chip sustains outside the logprob kernels (include/rlk_probes.h):
+                a streaming read of the same 622 MB of logits (GB/s) and a register-only
+                bf16 MFMA loop on random operands (TFLOP/s); roofline.frac_of_probe and
+                fused.roofline.frac_of_probe state the kernels' rates against them.
 
 The MFMA-bound calls (fused, fused.configs, fused_backward) are timed after about 0.13 s of
 back-to-back warmup calls: after an idle gap the chip's clock takes ~30 ms of MFMA load to
@@ -54,6 +58,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_reduce_T1024_V151936_traffic.
 TRAFFIC_FILE_BF16 = os.path.join(ROOT, "profiles", "row_reduce_bf16_T1024_V151936_traffic.json")
 # Warmup calls of the fused path at T = 2048 (~0.13 s; see the module docstring).
 FUSED_WARMUP_CALLS = 60
+# MFMA probe: one workgroup per CU, ~5 ms per launch (20 warmup launches, 5 timed).
+MFMA_PROBE_BLOCKS = 256
+MFMA_PROBE_ITERS = 32768
 TRAFFIC_SOURCES = ["entropy_rlk_logprob_amd/csrc/rlk_logits.hip",
                    "entropy_rlk_logprob_amd/csrc/rlk_state.hpp"]
 
@@ -180,6 +187,18 @@ def main():
                 "traffic": traffic, "kernel": "row_reduce_kernel<float,8,true>",
                 "kernel_ms": round(k_ms, 5), "algorithmic_bytes": alg_bytes}
 
+    probes = binding.load_probes()
+    sink = torch.empty(probes.READ_BLOCKS * probes.THREADS, dtype=torch.float32, device="cuda")
+    log("timing the streaming-read probe")
+    r_ms, _ = time_calls(lambda: probes.stream_read(x, sink), 20, 5)
+    read_gbs = x.numel() * 4 / (r_ms / 1e3) / 1e9
+    ceilings = {"hbm_stream_read": {
+        "achieved": round(read_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(read_gbs / HBM_PEAK_GBS, 4),
+        "probe": "rlk_probe_stream_read: the 622 MB logits read once, 2048 x 256 threads, "
+                 "16-byte non-temporal loads"}}
+    roofline["frac_of_probe"] = round(achieved / read_gbs, 4)
+
     if args.copy_probe:
         dst = torch.empty_like(x)
         for _ in range(5):
@@ -290,6 +309,21 @@ def main():
                               "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                               "flops_per_call": flops}}
+        log("timing the MFMA probe")
+        msink = torch.empty(MFMA_PROBE_BLOCKS * probes.THREADS, dtype=torch.float32,
+                            device="cuda")
+        mflops = probes.mfma(MFMA_PROBE_BLOCKS, MFMA_PROBE_ITERS, msink)
+        m_ms, _ = time_calls(lambda: probes.mfma(MFMA_PROBE_BLOCKS, MFMA_PROBE_ITERS, msink),
+                             5, 20)
+        mtf = mflops / (m_ms / 1e3) / 1e12
+        ceilings["mfma_bf16"] = {
+            "achieved": round(mtf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(mtf / BF16_PEAK_TFLOPS, 4),
+            "probe": "rlk_probe_mfma: register-only v_mfma_f32_32x32x16_bf16, 8 accumulators "
+                     "per wave, random bf16 operands rotated every step, one workgroup of 4 "
+                     "waves per CU"}
+        fused["roofline"]["frac_of_probe"] = round(tflops / mtf, 4)
+        fused_backward["roofline"]["frac_of_probe"] = round(btf / mtf, 4)
         fused_configs = {S.WORKLOADS[4].name: {"ms_per_call": fused["ms_per_call"],
                                                "frac": fused["roofline"]["frac"]}}
         if not args.no_fused_configs:
@@ -327,7 +361,7 @@ def main():
                    "parallelism": "single-gpu"},
         "backend": lib.backend_id(),
         "roofline": roofline, "cpu_baseline": cpu, "fused": fused, "fused_backward": fused_backward, "splits_ms": splits,
-        "bf16_logits": bf16, "backward": backward,
+        "bf16_logits": bf16, "backward": backward, "ceilings": ceilings,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)

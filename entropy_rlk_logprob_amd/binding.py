@@ -15,6 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB_PATH = os.path.join(PKG, "librlk_logprob.so")
 HEADER = os.path.join(ROOT, "include", "rlk_logprob.h")
+PROBES_PATH = os.path.join(PKG, "librlk_probes.so")
+PROBES_HEADER = os.path.join(ROOT, "include", "rlk_probes.h")
 
 RLK_OK = 0
 RLK_ERR_INVALID_ARGUMENT = 1
@@ -53,9 +55,9 @@ _c_i64 = ctypes.c_int64
 _c_p = ctypes.c_void_p
 
 
-def header_functions() -> list[str]:
-    """Names of the functions include/rlk_logprob.h declares."""
-    with open(HEADER) as f:
+def header_functions(header: str = HEADER) -> list[str]:
+    """Names of the functions a header (default include/rlk_logprob.h) declares."""
+    with open(header) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z_0-9]*\s*\*?\s*(rlk_[a-z0-9_]+)\s*\(",
@@ -403,3 +405,50 @@ def load(path: str = LIB_PATH) -> Library:
     if _LIB is None or _LIB.path != path:
         _LIB = Library(path)
     return _LIB
+
+
+class Probes:
+    """The measurement probes of include/rlk_probes.h (librlk_probes.so), for bench.py."""
+
+    READ_BLOCKS, THREADS = 2048, 256
+
+    def __init__(self, path: str = PROBES_PATH):
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m entropy_rlk_logprob_amd.build`")
+        import torch  # noqa: F401  (bind to torch's HIP runtime first, as Library does)
+        self.lib = ctypes.CDLL(path)
+        vp, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+        self.lib.rlk_probe_stream_read.argtypes = [vp, sz, vp, vp]
+        self.lib.rlk_probe_stream_read.restype = ctypes.c_int
+        self.lib.rlk_probe_mfma.argtypes = [i32, i32, u32, vp, vp]
+        self.lib.rlk_probe_mfma.restype = ctypes.c_int
+
+    @staticmethod
+    def _stream(dev):
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def stream_read(self, buf, sink):
+        """Reads all bytes of the contiguous CUDA tensor `buf`; sink: >= 2048 * 256 floats."""
+        _require(buf.is_contiguous() and buf.is_cuda, "buf must be a contiguous CUDA tensor")
+        _require(sink.numel() >= self.READ_BLOCKS * self.THREADS, "sink too small")
+        nbytes = buf.numel() * buf.element_size()
+        st = self.lib.rlk_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                            ctypes.c_void_p(sink.data_ptr()),
+                                            self._stream(buf.device))
+        if st != 0:
+            raise RuntimeError(f"rlk_probe_stream_read failed ({st})")
+        return nbytes
+
+    def mfma(self, blocks: int, iters: int, sink, seed: int = 1):
+        """Returns the flops of one launch; sink: >= blocks * 256 floats."""
+        _require(sink.numel() >= blocks * self.THREADS, "sink too small")
+        st = self.lib.rlk_probe_mfma(blocks, iters, seed, ctypes.c_void_p(sink.data_ptr()),
+                                     self._stream(sink.device))
+        if st != 0:
+            raise RuntimeError(f"rlk_probe_mfma failed ({st})")
+        return blocks * 4 * iters * 8 * 32768.0
+
+
+def load_probes(path: str = PROBES_PATH) -> Probes:
+    return Probes(path)

@@ -1,4 +1,5 @@
-"""Build librlk_logprob.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+"""Build librlk_logprob.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree, and the
+measurement probes of bench.py (librlk_probes.so, include/rlk_probes.h).
 
     python -m entropy_rlk_logprob_amd.build [--verbose]
 
@@ -21,6 +22,8 @@ LIB_NAME = "librlk_logprob.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["rlk_api.hip", "rlk_logits.hip", "rlk_linear.hip", "rlk_compare.hip", "rlk_backward.hip",
            "rlk_linear_bwd.hip"]
+PROBES_SOURCE = "rlk_probes.hip"
+PROBES_PATH = os.path.join(PKG, "librlk_probes.so")
 ARCH = "gfx950"
 
 
@@ -42,9 +45,15 @@ def flags() -> list[str]:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source into one shared library; returns its path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
+    """Compile every source into the logprob library, then the probe library; returns the
+    logprob library's path."""
+    _compile([os.path.join(CSRC, s) for s in SOURCES], LIB_PATH, verbose)
+    _compile([os.path.join(CSRC, PROBES_SOURCE)], PROBES_PATH, verbose)
+    return LIB_PATH
+
+
+def _compile(srcs: list[str], out: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc()] + flags() + srcs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -56,8 +65,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
 
 
 if __name__ == "__main__":

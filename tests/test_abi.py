@@ -42,6 +42,23 @@ def test_exports_every_header_symbol(L):
         assert ctypes.cast(getattr(L.lib, n), ctypes.c_void_p).value
 
 
+def test_probe_library_exports_its_header():
+    """librlk_probes.so (the benchmark's measurement probes) exports what
+    include/rlk_probes.h declares and rejects bad arguments without launching."""
+    names = B.header_functions(B.PROBES_HEADER)
+    assert set(names) == {"rlk_probe_stream_read", "rlk_probe_mfma"}
+    P = B.load_probes()
+    for n in names:
+        assert ctypes.cast(getattr(P.lib, n), ctypes.c_void_p).value
+    vp = ctypes.c_void_p
+    assert P.lib.rlk_probe_stream_read(None, 1024, vp(FAKE), None) == -1
+    assert P.lib.rlk_probe_stream_read(vp(FAKE), 1000, vp(FAKE), None) == -1     # not 16 B
+    assert P.lib.rlk_probe_stream_read(vp(FAKE + 8), 1024, vp(FAKE), None) == -1  # misaligned
+    assert P.lib.rlk_probe_mfma(0, 4, 1, vp(FAKE), None) == -1
+    assert P.lib.rlk_probe_mfma(1, 6, 1, vp(FAKE), None) == -1                    # iters % 4
+    assert P.lib.rlk_probe_mfma(1, 4, 1, None, None) == -1
+
+
 def test_backend_and_status_strings(L):
     assert L.backend_id() == "rlk.logprob.strict.gfx950.v1"
     for st in range(5):
