@@ -87,8 +87,9 @@ typedef struct {
 
 /*
  * Device workspace, in bytes, that the call `op` needs for these sizes.  Pure host
- * arithmetic (no device access).  `hidden` is ignored unless op == RLK_OP_LINEAR;
- * for RLK_OP_COMPARE only n_tokens is used (vocab, hidden, vocab_splits are ignored).
+ * arithmetic (no device access).  `hidden` is ignored unless op is RLK_OP_LINEAR or
+ * RLK_OP_LINEAR_BACKWARD; for RLK_OP_COMPARE only n_tokens is used (vocab, hidden,
+ * vocab_splits are ignored).
  * The workspace must be 256-byte aligned; its contents on entry do not matter.
  * Returns RLK_ERR_INVALID_ARGUMENT for a bad op, negative sizes or a bad split count.
  */
@@ -252,6 +253,7 @@ rlk_status rlk_linear_logprob_backward(const uint16_t* hidden_bf16, int64_t ld_h
  *                   call; unlike the other calls, n_tokens == 0 still launches one small
  *                   kernel, to write the all-zero result
  *   workspace       rlk_workspace_bytes(RLK_OP_COMPARE, n_tokens, ...) bytes, 256-aligned
+ * Sizes: 0 <= n_tokens <= 2^40.
  * Deterministic: fixed token-to-thread mapping and a fixed combination tree, no atomics;
  * the same inputs give the same bits on every call.
  */
