@@ -360,7 +360,8 @@ def main():
                    "vocab_splits": 1, "temperature": 1.0, "logits_dtype": "f32",
                    "parallelism": "single-gpu"},
         "backend": lib.backend_id(),
-        "roofline": roofline, "cpu_baseline": cpu, "fused": fused, "fused_backward": fused_backward, "splits_ms": splits,
+        "roofline": roofline, "cpu_baseline": cpu, "fused": fused,
+        "fused_backward": fused_backward, "splits_ms": splits,
         "bf16_logits": bf16, "backward": backward, "ceilings": ceilings,
         "device": torch.cuda.get_device_name(0),
     }

@@ -8,7 +8,8 @@
 // configurations ask for a deterministic gradient).
 //
 // Pass 1 is the forward row reducer (canonical order, any vocab split) writing each row's
-// root state (m, s, u) -- skipped when the caller passes the states its forward call saved.  Pass 2, below, streams the row again: per element
+// root state (m, s, u) -- skipped when the caller passes the states its forward call
+// saved.  Pass 2, below, streams the row again: per element
 //   a = c (x - m)          (fp32, as in the forward leaf),   q = a - log2 s,
 //   p = 2^q,  ln p = q ln 2,
 //   grad = beta (g_lp (delta_it - p) - g_ent p (ln p + H)),

@@ -392,9 +392,10 @@ hipError_t launch_linear_backward(const LinearArgs& fwd, const float* g_lp, cons
   if (dW) {
     // dW[v, k] = sum_t dX^T[v, t] H^T[k, t]: A = dX^T (M = V), B = H^T (N = d; a transposed
     // copy of H, small), both K-contiguous, K = Tp; row-tile-major within groups of 8
-    // column tiles, so that the tiles sharing a dX^T slice run together; stored row-major (32 lanes write 128 contiguous
-    // bytes of a dW row).  (Reading dX in place as a K-major A operand measured 0.6 ms
-    // slower at T = 2048, d = 4096, V = 151936 than writing dX^T in step 3.)
+    // column tiles, so that the tiles sharing a dX^T slice run together; stored row-major
+    // (32 lanes write 128 contiguous bytes of a dW row).  (Reading dX in place as a K-major
+    // A operand measured 0.6 ms slower at T = 2048, d = 4096, V = 151936 than writing dX^T
+    // in step 3.)
     uint16_t* ht = reinterpret_cast<uint16_t*>(base + L.ht);
     hipLaunchKernelGGL(transpose_pad_kernel, split_grid(L.Tp / 64, (unsigned)(d / 64)),
                        dim3(256), 0, stream, a.H, a.ldh, T, d, ht, L.Tp, L.Tp);

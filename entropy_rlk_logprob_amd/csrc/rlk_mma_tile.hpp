@@ -273,10 +273,11 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
 
 // Workgroup id -> (row tile, column tile) of an n_rt x n_ct grid of output tiles, launched
 // as split_grid(8 ceil(n_rt n_ct / 8)).  The hardware hands workgroup ids out round-robin
-// over the 8 XCDs; the remap gives each XCD a contiguous range of logical tiles.  Logical tiles run one group of up to G column tiles
-// at a time, row-tile-major within the group, so that the ~32 tiles an XCD runs at once
-// are a few row tiles times one column group and share both operands' slices in that
-// XCD's L2.  Returns false for the padding ids beyond the grid.
+// over the 8 XCDs; the remap gives each XCD a contiguous range of logical tiles.  Logical
+// tiles run one group of up to G column tiles at a time, row-tile-major within the group,
+// so that the ~32 tiles an XCD runs at once are a few row tiles times one column group and
+// share both operands' slices in that XCD's L2.  Returns false for the padding ids beyond
+// the grid.
 template <int G>
 __device__ __forceinline__ bool grouped_tile_of(int64_t n_rt, int64_t n_ct, int64_t& rt,
                                                 int64_t& ct) {
