@@ -95,6 +95,29 @@ def test_out_of_range_targets_and_empty(lib):
     assert lp0.numel() == 0 and ent0.numel() == 0
 
 
+def test_nonfinite_inputs_follow_the_logit_rules(lib):
+    """Non-finite bf16 inputs: a NaN in a hidden row makes that row's logits NaN; +inf in
+    W[7, 3] makes logit 7 of token r +inf, -inf or NaN as h[r, 3] is > 0, < 0 or 0 (fp32
+    accumulation, as the fp64 oracle forms them).  The logit rules then give NaN rows, and
+    for -inf a token of probability zero (logprob -inf where it is the target)."""
+    T, d, V = 40, 64, 3000
+    announce("linear non-finite inputs")
+    case = S.random_fused_case(T, d, V, seed=9200, w_sigma=0.3)
+    h, w = case.h_bits.copy(), case.w_bits.copy()
+    h[0, 5] = 0x7FC0                     # NaN
+    w[7, 3] = 0x7F80                     # +inf
+    h[1, 3] = 0x0000                     # inf * 0 -> NaN logit
+    t = case.targets.copy()
+    t[2::3] = 7
+    olp, oent = oracle.linear_logprob_entropy(f32(h), f32(w), t)
+    lp, ent = run_linear(lib, h, w, t)
+    assert np.isnan(lp[0]) and np.isnan(lp[1])
+    assert np.isnan(olp).any() and np.isfinite(oent).any() and np.isneginf(olp).any()
+    assert max_abs(lp, olp) <= TOL_LINEAR and max_abs(ent, oent) <= TOL_LINEAR
+    lp4, ent4 = run_linear(lib, h, w, t, 1.0, 4)
+    assert bitwise_equal(lp4, lp) and bitwise_equal(ent4, ent)
+
+
 @pytest.fixture(scope="module")
 def cfg3():
     announce("generating fused workload T=1024 d=2048 V=151936")
