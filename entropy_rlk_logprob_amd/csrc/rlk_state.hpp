@@ -95,8 +95,7 @@ __device__ __forceinline__ WireState to_wire(const State& s, float xt) {
 
 // x * y with 0 * (anything) = 0 (v_mul_legacy_f32): a zero-probability term (2^a = 0 at
 // a = -inf) then adds nothing to u instead of 0 * (-inf) = NaN.  Otherwise equal to x * y.
-__device__ __attribute__((const, noconvergent)) float mul_zero_wins(float, float) __asm(
-    "llvm.amdgcn.fmul.legacy");
+__device__ __attribute__((const, noconvergent)) float mul_zero_wins(float, float) __asm("llvm.amdgcn.fmul.legacy");
 
 // Leaf of 16 fp32 values v[0..15] (four quads of four): exact max m, then the fp32 terms
 // 2^a and 2^a * a with a = c (v - m) summed pairwise, within each quad and then across
