@@ -217,13 +217,60 @@ __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
 // The tile tree is the perfect binary tree over tile index, padded with identity states up
 // to P = max(8, next power of two >= tiles per chunk) leaves (merging a state with the
 // identity on its right returns it unchanged, up to the sign of a zero u).  A wave serves
-// 8 consecutive tokens x 8 aligned blocks of P / 8 tiles: lane = 8 blk + token, so each
+// 8 consecutive tokens x 8 aligned blocks of B = P / 8 tiles: lane = 8 blk + token, so each
 // load instruction reads 8 runs of 8 consecutive tokens' states (192 bytes each).  A lane
-// folds its block with a binary-counter stack (identities elided) -- the subtree of that
-// block -- and an xor-butterfly over the block bits (strides 8, 16, 32; lower block first)
-// applies the top three levels.  Block: CPS waves (the shard's chunks); grid
-// (ceil(T / 8), S).
-template <int CPS>
+// reduces its block -- the subtree of that block, identities elided -- and an xor-butterfly
+// over the block bits (strides 8, 16, 32; lower block first) applies the top three levels.
+// Block: CPS waves (the shard's chunks); grid (ceil(T / 8), S).
+//
+// LB = log2 B when B <= 16 (every vocabulary up to 8 * 128 * 256 = 262144): the lane issues
+// all B loads at once and reduces them level by level in registers.  LB = kStackLB for
+// larger blocks: one load at a time, folded into a binary-counter stack.  Both evaluate the
+// same tree, so they give the same bits.
+constexpr int kStackLB = 5;
+
+// Subtree of leaves [k0, k1) of a block of 2^LB, k0 < k1 <= k0 + 2^LB; a right subtree with
+// no leaves is elided (its parent is its left subtree).
+template <int LB>
+__device__ __forceinline__ State block_subtree(const WireState* __restrict__ base, int64_t k0,
+                                               int64_t k1, int64_t stride, float c) {
+  constexpr int B = 1 << LB;
+  const int n = (int)(k1 - k0);
+  State v[B];
+#pragma unroll
+  for (int i = 0; i < B; ++i) {
+    // Leaves past the end re-read the last one (in bounds); they are never merged.
+    const int64_t k = k0 + min(i, n - 1);
+    v[i] = from_wire(base[k * stride]);
+  }
+#pragma unroll
+  for (int w = B / 2; w >= 1; w /= 2) {
+    const int span = B / w / 2;  // leaves under each child at this level
+#pragma unroll
+    for (int i = 0; i < w; ++i)
+      if ((2 * i + 1) * span < n) v[i] = rlk_merge(v[2 * i], v[2 * i + 1], c);
+      else v[i] = v[2 * i];
+  }
+  return v[0];
+}
+
+template <>
+__device__ __forceinline__ State block_subtree<kStackLB>(const WireState* __restrict__ base,
+                                                         int64_t k0, int64_t k1, int64_t stride,
+                                                         float c) {
+  State stk[kMaxTreeDepth];
+  int top = 0;
+  for (int64_t k = k0; k < k1; ++k) {
+    State cur = from_wire(base[k * stride]);
+    for (int64_t b = k - k0; b & 1; b >>= 1) cur = rlk_merge(stk[--top], cur, c);
+    stk[top++] = cur;
+  }
+  State r = stk[--top];
+  while (top > 0) r = rlk_merge(stk[--top], r, c);
+  return r;
+}
+
+template <int CPS, int LB>
 __global__ __launch_bounds__(64 * CPS) void tile_tree_kernel(
     const WireState* __restrict__ tile_states, const float* __restrict__ target_logit,
     TileGeom g, const int64_t* __restrict__ targets, float c, double beta,
@@ -241,18 +288,8 @@ __global__ __launch_bounds__(64 * CPS) void tile_tree_kernel(
   const int64_t k0 = (int64_t)blk * g.block_tiles;
   const int64_t k1 = min(k0 + g.block_tiles, g.tpc);
   State r = identity_state();
-  if (tok < g.T && k0 < k1) {
-    const WireState* __restrict__ base = tile_states + chunk * g.tpc * g.T + tok;
-    State stk[kMaxTreeDepth];
-    int top = 0;
-    for (int64_t k = k0; k < k1; ++k) {
-      State cur = from_wire(base[k * g.T]);
-      for (int64_t b = k - k0; b & 1; b >>= 1) cur = rlk_merge(stk[--top], cur, c);
-      stk[top++] = cur;
-    }
-    r = stk[--top];
-    while (top > 0) r = rlk_merge(stk[--top], r, c);
-  }
+  if (tok < g.T && k0 < k1)
+    r = block_subtree<LB>(tile_states + chunk * g.tpc * g.T + tok, k0, k1, g.T, c);
 #pragma unroll
   for (int off = 8; off < 64; off <<= 1) {
     const State o = shfl_xor_state(r, off);
@@ -282,6 +319,26 @@ __global__ __launch_bounds__(64 * CPS) void tile_tree_kernel(
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// tile_tree_kernel for a shard of CPS chunks and blocks of 2^lb tiles (the stack form above 16).
+template <int CPS>
+void launch_tile_tree(int lb, dim3 grid, hipStream_t stream, const WireState* tiles,
+                      const float* tl, const TileGeom& g, const int64_t* targets, float c,
+                      double beta, float* lp, float* ent, WireState* sws, WireState* root) {
+  const dim3 block(64 * CPS);
+#define RLK_TREE(L)                                                                          \
+  hipLaunchKernelGGL((tile_tree_kernel<CPS, L>), grid, block, 0, stream, tiles, tl, g, targets, \
+                     c, beta, lp, ent, sws, root)
+  switch (lb) {
+    case 0: RLK_TREE(0); break;
+    case 1: RLK_TREE(1); break;
+    case 2: RLK_TREE(2); break;
+    case 3: RLK_TREE(3); break;
+    case 4: RLK_TREE(4); break;
+    default: RLK_TREE(kStackLB); break;
+  }
+#undef RLK_TREE
+}
 
 }  // namespace
 
@@ -328,22 +385,24 @@ hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream) {
   const float* tl = reinterpret_cast<const float*>(base + L.target_logit);
   WireState* sws = reinterpret_cast<WireState*>(base + L.shard_states);
   const dim3 tgrid = split_grid((a.T + 7) / 8, (unsigned)a.S);
+  int lb = 0;
+  while ((int64_t(1) << lb) < g.block_tiles) ++lb;
   switch (a.S) {
     case 1:
-      hipLaunchKernelGGL((tile_tree_kernel<8>), tgrid, dim3(512), 0, stream, tiles, tl, g,
-                         a.targets, a.c, a.beta, a.lp, a.ent, sws, a.root);
+      launch_tile_tree<8>(lb, tgrid, stream, tiles, tl, g, a.targets, a.c, a.beta, a.lp, a.ent,
+                          sws, a.root);
       return hipGetLastError();
     case 2:
-      hipLaunchKernelGGL((tile_tree_kernel<4>), tgrid, dim3(256), 0, stream, tiles, tl, g,
-                         a.targets, a.c, a.beta, a.lp, a.ent, sws, a.root);
+      launch_tile_tree<4>(lb, tgrid, stream, tiles, tl, g, a.targets, a.c, a.beta, a.lp, a.ent,
+                          sws, a.root);
       break;
     case 4:
-      hipLaunchKernelGGL((tile_tree_kernel<2>), tgrid, dim3(128), 0, stream, tiles, tl, g,
-                         a.targets, a.c, a.beta, a.lp, a.ent, sws, a.root);
+      launch_tile_tree<2>(lb, tgrid, stream, tiles, tl, g, a.targets, a.c, a.beta, a.lp, a.ent,
+                          sws, a.root);
       break;
     case 8:
-      hipLaunchKernelGGL((tile_tree_kernel<1>), tgrid, dim3(64), 0, stream, tiles, tl, g,
-                         a.targets, a.c, a.beta, a.lp, a.ent, sws, a.root);
+      launch_tile_tree<1>(lb, tgrid, stream, tiles, tl, g, a.targets, a.c, a.beta, a.lp, a.ent,
+                          sws, a.root);
       break;
     default:
       return hipErrorInvalidValue;
