@@ -153,7 +153,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(vocab splits are emulated on one GPU); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
