@@ -50,6 +50,26 @@ def test_shapes_vs_oracle_and_split_bitwise(lib, T, d, V, tau):
             assert bitwise_equal(lp, ref[0]) and bitwise_equal(ent, ref[1]), split
 
 
+@pytest.mark.parametrize("V", [33563, 65536, 65600, 131065, 131392, 262144, 262176])
+def test_tile_tree_block_sizes(lib, V):
+    """The chunk's tile tree is reduced in blocks of P / 8 tiles (P: tiles per chunk rounded
+    up to a power of two): in registers for blocks of 4, 8 and 16 tiles, by a stack beyond.
+    These vocabularies put 17, 32, 33, 64, 65, 128 and 129 tiles in a chunk, i.e. each block
+    size with a full and a partly empty last block, and the first stack case."""
+    T, d = 9, 64
+    announce(f"linear T={T} d={d} V={V} (tile tree blocks)")
+    case = S.random_fused_case(T, d, V, seed=9200 + V % 1000, h_sigma=1.0,
+                               w_sigma=3.0 / math.sqrt(d))
+    olp, oent = oracle.linear_logprob_entropy(f32(case.h_bits), f32(case.w_bits), case.targets,
+                                              1.0)
+    h, w, t = bits_dev(case.h_bits), bits_dev(case.w_bits), dev(case.targets)
+    lp, ent = run_linear(lib, h, w, t)
+    assert max_abs(lp, olp) <= TOL_LINEAR and max_abs(ent, oent) <= TOL_LINEAR
+    for split in (2, 8):
+        lps, ents = run_linear(lib, h, w, t, 1.0, split)
+        assert bitwise_equal(lps, lp) and bitwise_equal(ents, ent), split
+
+
 def test_token_tile_groups_with_partial_last_group(lib):
     """T = 2600: 11 token tiles, which the kernel runs as a group of 8 and a partial group
     of 3.  Every row against the oracle; the rows of the partial group alone, and vocab
