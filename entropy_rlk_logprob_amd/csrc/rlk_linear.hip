@@ -59,6 +59,9 @@ struct TileGeom {
 // MFMA block): m = their max, then fp32 terms 2^{c (x - m)} and 2^{c (x - m)} c (x - m)
 // summed pairwise -- within each quad, quad pairs, then the groups as ((0,1),(2,3)).
 // With every value in registers the max comes first and no state merge is needed.
+// WITH_U = false (no entropy or row state requested) leaves u at 0 and skips its terms;
+// m and s, and so every logprob bit, are the same either way.
+template <bool WITH_U>
 __device__ __forceinline__ State leaf64(const float (&v)[4][16], float c) {
   float mg = v[0][0];
 #pragma unroll
@@ -74,24 +77,25 @@ __device__ __forceinline__ State leaf64(const float (&v)[4][16], float c) {
     for (int i = 0; i < 16; ++i) {
       const float x = (v[a][i] - mref) * c;
       e[i] = exp2_hw(x);
-      t[i] = mul_zero_wins(e[i], x);  // 0 where e = 0 (a masked row)
+      if constexpr (WITH_U) t[i] = mul_zero_wins(e[i], x);  // 0 where e = 0 (a masked row)
     }
     float sq[4], uq[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       sq[j] = (e[4 * j] + e[4 * j + 1]) + (e[4 * j + 2] + e[4 * j + 3]);
-      uq[j] = (t[4 * j] + t[4 * j + 1]) + (t[4 * j + 2] + t[4 * j + 3]);
+      if constexpr (WITH_U) uq[j] = (t[4 * j] + t[4 * j + 1]) + (t[4 * j + 2] + t[4 * j + 3]);
     }
     sg[a] = (sq[0] + sq[1]) + (sq[2] + sq[3]);
-    ug[a] = (uq[0] + uq[1]) + (uq[2] + uq[3]);
+    if constexpr (WITH_U) ug[a] = (uq[0] + uq[1]) + (uq[2] + uq[3]);
   }
   State r;
   r.m = mg;
   r.s = (double)((sg[0] + sg[1]) + (sg[2] + sg[3]));
-  r.u = (double)((ug[0] + ug[1]) + (ug[2] + ug[3]));
+  r.u = WITH_U ? (double)((ug[0] + ug[1]) + (ug[2] + ug[3])) : 0.0;
   return r;
 }
 
+template <bool WITH_U>
 __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
     const uint16_t* __restrict__ H, int64_t ldh, const uint16_t* __restrict__ W, int64_t ldw,
     int64_t d, TileGeom g, const int64_t* __restrict__ targets, float c,
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
             v[a][i] = (vr < n_valid) ? v[a][i] : kNegInf;
           }
         }
-      const State st = leaf64(v, c);
+      const State st = leaf64<WITH_U>(v, c);
       const State o = shfl_xor_state(st, 32);
       half_state[b] = fhalf ? rlk_merge(o, st, c) : rlk_merge(st, o, c);
     }
@@ -374,10 +378,17 @@ hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream) {
   char* base = static_cast<char*>(a.ws);
   const int64_t nb = g.n_vt * g.n_tt;
   const int64_t nb_pad = ((nb + 7) / 8) * 8;
-  hipLaunchKernelGGL(linear_tile_kernel, split_grid(nb_pad), dim3(kThreads), 0, stream, a.H,
-                     a.ldh, a.W, a.ldw, a.d, g, a.targets, a.c,
-                     reinterpret_cast<WireState*>(base + L.tile_states),
-                     reinterpret_cast<float*>(base + L.target_logit));
+  // Entropy terms only when an entropy or a row state is asked for.
+  if (a.ent || a.root)
+    hipLaunchKernelGGL(linear_tile_kernel<true>, split_grid(nb_pad), dim3(kThreads), 0, stream,
+                       a.H, a.ldh, a.W, a.ldw, a.d, g, a.targets, a.c,
+                       reinterpret_cast<WireState*>(base + L.tile_states),
+                       reinterpret_cast<float*>(base + L.target_logit));
+  else
+    hipLaunchKernelGGL(linear_tile_kernel<false>, split_grid(nb_pad), dim3(kThreads), 0, stream,
+                       a.H, a.ldh, a.W, a.ldw, a.d, g, a.targets, a.c,
+                       reinterpret_cast<WireState*>(base + L.tile_states),
+                       reinterpret_cast<float*>(base + L.target_logit));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 

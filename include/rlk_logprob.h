@@ -147,6 +147,8 @@ rlk_status rlk_entropy_bf16(const uint16_t* logits, int64_t ld_logits, int64_t n
  *                 hidden_dim, multiples of 8 and at most 2^22; both base pointers
  *                 16-byte aligned; vocab at most 2^26
  *   other arguments as rlk_logprob_from_logits; entropy_out and row_states_out may be NULL
+ *                 (with both NULL the tiles skip the entropy terms: the logprob bits are the
+ *                 same as with them)
  */
 rlk_status rlk_linear_logprob(const uint16_t* hidden_bf16, int64_t ld_hidden,
                               const uint16_t* weight_bf16, int64_t ld_weight, int64_t n_tokens,

@@ -70,6 +70,24 @@ def test_tile_tree_block_sizes(lib, V):
         assert bitwise_equal(lps, lp) and bitwise_equal(ents, ent), split
 
 
+@pytest.mark.parametrize("T,d,V,split", [(37, 128, 1000, 1), (300, 256, 20000, 4),
+                                          (64, 512, 151936, 1), (257, 64, 2049, 8)])
+def test_logprob_only_calls_give_the_same_bits(lib, T, d, V, split):
+    """Without an entropy output (and no row states) the tiles skip the entropy terms; the
+    logprob depends only on each state's max and sum, so its bits must not change."""
+    import torch
+    announce(f"linear logprob only T={T} d={d} V={V} split={split}")
+    case = S.random_fused_case(T, d, V, seed=9300 + T, h_sigma=1.0, w_sigma=3.0 / math.sqrt(d),
+                               temperature=0.7)
+    h, w, t = bits_dev(case.h_bits), bits_dev(case.w_bits), dev(case.targets)
+    lp, ent = run_linear(lib, h, w, t, 0.7, split)
+    lp_only, none = lib.linear_logprob(h, w, t, 0.7, split, with_entropy=False)
+    torch.cuda.synchronize()
+    assert none is None and bitwise_equal(lp_only.cpu().numpy(), lp)
+    olp, _ = oracle.linear_logprob_entropy(f32(case.h_bits), f32(case.w_bits), case.targets, 0.7)
+    assert max_abs(lp, olp) <= TOL_LINEAR
+
+
 def test_token_tile_groups_with_partial_last_group(lib):
     """T = 2600: 11 token tiles, which the kernel runs as a group of 8 and a partial group
     of 3.  Every row against the oracle; the rows of the partial group alone, and vocab

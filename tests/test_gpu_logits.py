@@ -139,6 +139,17 @@ def test_entropy_call_matches_entropy_output(lib, cfg2):
         assert bitwise_equal(ent.cpu().numpy(), ref_ent)
 
 
+def test_logprob_only_calls_give_the_same_bits(lib, cfg2):
+    import torch
+    _, _, _, xd, td = cfg2
+    ref_lp, _ = run_logits(lib, xd, td, 0.7, 1)
+    for split in (1, 4):
+        announce(f"logits logprob only T=1024 split={split}")
+        lp, none = lib.logprob_from_logits(xd, td, 0.7, split, with_entropy=False)
+        torch.cuda.synchronize()
+        assert none is None and bitwise_equal(lp.cpu().numpy(), ref_lp)
+
+
 def test_closed_forms(lib):
     announce("logits closed forms")
     for V in (1, 2, 1024, 151936):
