@@ -15,7 +15,8 @@ Also reported on the same JSON line:
                 V = 151936 bf16) as tokens/s and fraction of the 2.5 PFLOP/s bf16
                 MFMA peak (2 T V d flops per call); fused.configs adds the Qwen3-Next
                 shape (T = 1024, d = 2048) and the large ragged batch (T = 16384,
-                d = 4096, temperature 0.7);
+                d = 4096, temperature 0.7); fused.logprob_only times the same call
+                without the entropy output;
   splits        ms per call of the logits path at vocab splits 2, 4, 8;
   bf16_logits   the same rows rounded to bf16 through rlk_logprob_from_logits_bf16
                 (1024 x 303888 B per call) as GB/s against 8 TB/s;
@@ -273,6 +274,10 @@ def main():
         fsteps = max(5, min(args.steps, 20))
         log(f"timing fused path: steps {fsteps}")
         f_ms, f_wall = time_calls(fstep, fsteps, FUSED_WARMUP_CALLS)
+        log("timing fused path, logprob only")
+        flo_ms, _ = time_calls(
+            lambda: lib.linear_logprob(h, w, tt, 1.0, 1, with_entropy=False, out=(flp, None),
+                                       workspace=fws), fsteps, 5)
         log("timing fused backward")
         fgl = torch.randn(Tf, generator=torch.Generator().manual_seed(9)).cuda()
         fge = torch.randn(Tf, generator=torch.Generator().manual_seed(10)).cuda()
@@ -308,7 +313,10 @@ def main():
                  "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                               "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                              "flops_per_call": flops}}
+                              "flops_per_call": flops},
+                 "logprob_only": {"ms_per_call": round(flo_ms, 4),
+                                  "frac": round(flops / (flo_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
+                                                4)}}
         log("timing the MFMA probe")
         msink = torch.empty(MFMA_PROBE_BLOCKS * probes.THREADS, dtype=torch.float32,
                             device="cuda")
