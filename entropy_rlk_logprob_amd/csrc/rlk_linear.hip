@@ -215,6 +215,128 @@ __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
   }
 }
 
+// Batches of at most 128 tokens: one workgroup takes a pair of consecutive vocabulary tiles
+// of a chunk (tiles 2p and 2p + 1, the second absent when the chunk has an odd count) as a
+// 512 x 128 output tile, so that half the workgroups do the same MFMA work as 256 x 256
+// tiles whose tokens would be mostly padding.  Each wave still holds 128 vocabulary rows x 64
+// tokens at the same places within its tile, and each tile's state is formed exactly as in
+// linear_tile_kernel (same leaves, same merges), so the bits are the same.
+template <bool WITH_U>
+__global__ __launch_bounds__(kThreads, 1) void linear_pair_kernel(
+    const uint16_t* __restrict__ H, int64_t ldh, const uint16_t* __restrict__ W, int64_t ldw,
+    int64_t d, TileGeom g, const int64_t* __restrict__ targets, float c,
+    WireState* __restrict__ tile_states, float* __restrict__ target_logit) {
+  constexpr int kPairStage = (2 * kTileV + 128) * kBK * 2;  // 80 KiB
+  __shared__ __attribute__((aligned(16))) char smem[2 * kPairStage];
+  const int64_t pp = (g.tpc + 1) / 2;  // pairs per chunk
+  int64_t pr, tt;
+  if (!mma::grouped_tile_of<8>(8 * pp, 1, pr, tt)) return;
+  const int64_t chunk = pr / pp;
+  const int64_t k0 = 2 * (pr % pp);
+  const bool has_second = k0 + 1 < g.tpc;
+  const int64_t vt0 = chunk * g.tpc + k0;
+  const int64_t chunk_lo = min(chunk * g.Vc, g.V);
+  const int64_t chunk_hi = min(chunk_lo + g.Vc, g.V);
+  const int64_t v_lo = chunk_lo + k0 * kTileV;
+  const int n_pair = (int)max((int64_t)0, min(v_lo + 2 * (int64_t)kTileV, chunk_hi) - v_lo);
+  if (n_pair == 0) {
+    // Empty tiles (short chunk): identity states so that the tile tree sees no data.
+    for (int j = threadIdx.x; j < 2 * 128; j += kThreads) {
+      const int pt = j >> 7;
+      const int64_t tok = j & 127;
+      if (tok < g.T && (pt == 0 || has_second))
+        tile_states[(vt0 + pt) * g.T + tok] = to_wire(identity_state(), 0.0f);
+    }
+    return;
+  }
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wv = wave >> 1;  // 128-row slice of the pair (0..3)
+  const int wt = wave & 1;   // token half (0, 1)
+  const int pt = wv >> 1;    // tile of the pair
+  const int hv = wv & 1;     // vocab half of that tile
+  const int64_t v_lo_t = v_lo + (int64_t)pt * kTileV;
+  const int n_valid = max(0, min(n_pair - pt * kTileV, kTileV));
+
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+  const int w_last = (int)min(g.V - 1 - v_lo, (int64_t)(2 * kTileV - 1));
+  const int h_last = (int)min(g.T - 1, (int64_t)127);
+  mma::mma_tile_op<false, false, 4>(mma::Operand{W + v_lo * ldw, ldw, w_last, 0},
+                                    mma::Operand{H, ldh, h_last, 0}, 0, (int)(d / kBK), smem,
+                                    acc);
+  __syncthreads();
+  const int frow = lane & 31;
+  const int fhalf = lane >> 5;
+
+  // Epilogue as in linear_tile_kernel, per tile of the pair: lane tokens wt*64 + b*32 +
+  // (lane%32), vocab rows hv*128 + a*32 + 8*(i/4) + 4*(lane/32) + (i%4) of tile pt.
+  State half_state[2];
+  auto token_epilogue = [&](auto masked) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int tok_in_tile = wt * 64 + b * 32 + frow;
+      const int64_t tok = tok_in_tile;
+      const int64_t tgt = (tok < g.T && targets) ? targets[tok] : -1;
+      const int tloc = (tgt >= v_lo_t && tgt < v_lo_t + n_valid) ? (int)(tgt - v_lo_t) : -1;
+      const int r = tloc - hv * 128;
+      const bool mine = tloc >= 0 && (unsigned)r < 128u && ((r >> 2) & 1) == fhalf;
+      if (mine) {
+        const int idx = ((r >> 5) << 4) | (((r >> 3) & 3) << 2) | (r & 3);  // 16 a + i
+        float xt = 0.0f;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xt = (idx == 16 * a + i) ? acc[a][b][i] : xt;
+        target_logit[tok] = xt;
+      }
+      float v[4][16];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          v[a][i] = acc[a][b][i];
+          if constexpr (decltype(masked)::value) {
+            const int vr = hv * 128 + a * 32 + 8 * (i >> 2) + 4 * fhalf + (i & 3);
+            v[a][i] = (vr < n_valid) ? v[a][i] : kNegInf;
+          }
+        }
+      const State st = leaf64<WITH_U>(v, c);
+      const State o = shfl_xor_state(st, 32);
+      half_state[b] = fhalf ? rlk_merge(o, st, c) : rlk_merge(st, o, c);
+    }
+  };
+  if (n_valid < kTileV)
+    token_epilogue(std::true_type{});
+  else
+    token_epilogue(std::false_type{});
+
+  State* xch = reinterpret_cast<State*>(smem);
+  if (hv == 1 && fhalf == 0) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) xch[pt * 128 + wt * 64 + b * 32 + frow] = half_state[b];
+  }
+  __syncthreads();
+  if (hv == 0 && fhalf == 0 && (pt == 0 || has_second)) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int tok_in_tile = wt * 64 + b * 32 + frow;
+      const int64_t tok = tok_in_tile;
+      if (tok < g.T) {
+        const State r = n_valid > 0 ? rlk_merge(half_state[b], xch[pt * 128 + tok_in_tile], c)
+                                    : identity_state();
+        tile_states[(vt0 + pt) * g.T + tok] = to_wire(r, 0.0f);
+      }
+    }
+  }
+}
+
 // Tiles of each chunk -> chunk state, chunks of a shard -> shard state (tree8), then
 // either the fp64 finalize (S = 1) or the shard's wire state for the cross-shard merge.
 //
@@ -379,7 +501,21 @@ hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream) {
   const int64_t nb = g.n_vt * g.n_tt;
   const int64_t nb_pad = ((nb + 7) / 8) * 8;
   // Entropy terms only when an entropy or a row state is asked for.
-  if (a.ent || a.root)
+  const bool with_u = a.ent || a.root;
+  if (a.T <= 128) {
+    const int64_t n_pairs = 8 * ((g.tpc + 1) / 2);
+    const dim3 pgrid = split_grid((n_pairs + 7) / 8 * 8);
+    if (with_u)
+      hipLaunchKernelGGL(linear_pair_kernel<true>, pgrid, dim3(kThreads), 0, stream, a.H, a.ldh,
+                         a.W, a.ldw, a.d, g, a.targets, a.c,
+                         reinterpret_cast<WireState*>(base + L.tile_states),
+                         reinterpret_cast<float*>(base + L.target_logit));
+    else
+      hipLaunchKernelGGL(linear_pair_kernel<false>, pgrid, dim3(kThreads), 0, stream, a.H, a.ldh,
+                         a.W, a.ldw, a.d, g, a.targets, a.c,
+                         reinterpret_cast<WireState*>(base + L.tile_states),
+                         reinterpret_cast<float*>(base + L.target_logit));
+  } else if (with_u)
     hipLaunchKernelGGL(linear_tile_kernel<true>, split_grid(nb_pad), dim3(kThreads), 0, stream,
                        a.H, a.ldh, a.W, a.ldw, a.d, g, a.targets, a.c,
                        reinterpret_cast<WireState*>(base + L.tile_states),

@@ -140,14 +140,20 @@ struct Operand {
 // Runs the K loop; the caller zeroes acc and, after the return (which waits for the
 // last DMA), issues a workgroup barrier before reusing smem.
 //   k0, nk  first K element (multiple of 8) and number of 64-wide K steps (>= 1)
-template <bool A_KMAJOR, bool B_KMAJOR>
+// WA = 4: a 512 x 128 tile instead (waves 4 (A side) x 2 (B side), each still 128 x 64;
+// K-contiguous operands only), with 80 KiB stages: for batches of at most 128 tokens.
+template <bool A_KMAJOR, bool B_KMAJOR, int WA = 2>
 __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, int64_t k0,
                                             int nk, char* smem, floatx16 (&acc)[4][2]) {
+  static_assert(WA == 2 || (WA == 4 && !A_KMAJOR && !B_KMAJOR), "512-row tiles: K-contiguous");
+  constexpr int kARows = 128 * WA;                   // 256 or 512
+  constexpr int kBRows = 64 * (8 / WA);              // 256 or 128
+  constexpr int kStage = (kARows + kBRows) * kBK * 2;  // 64 or 80 KiB
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wv = wave >> 2;  // A-side half (0, 1)
-  const int wt = wave & 3;   // B-side quarter (0..3)
+  const int wv = wave / (8 / WA);  // A-side 128-row slice (0, 1; or 0..3)
+  const int wt = wave % (8 / WA);  // B-side 64-row slice (0..3; or 0, 1)
   // Global -> LDS: direct 16-byte-per-lane loads into LDS (global_load_lds_dwordx4); one
   // wave instruction fills one 1 KiB block with lane l's 16 bytes at byte 16 l.  Blocks
   // 0..31 are the A slab, 32..63 the B slab; wave w fills blocks w, w + 8, ..., w + 56.
@@ -157,8 +163,8 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
   //     k row 2 b + l / 32 and so fetches logical column (l % 32) ^ (4 (k % 4)).
   // Offsets are tile-relative on workgroup-uniform bases; rows beyond the valid range
   // are clamped as Operand describes.
-  constexpr int kBlocksPerWave = (kTileV + kTileT) / 8 / (kThreads / 64);  // 8
-  constexpr int kWBlocks = kTileV / 8;
+  constexpr int kBlocksPerWave = (kARows + kBRows) / 8 / (kThreads / 64);  // 8 (WA = 4: 10)
+  constexpr int kWBlocks = kARows / 8;
   int64_t src_off[kBlocksPerWave];  // K-contiguous: offset at k = 0
   int kmaj_row[kBlocksPerWave];     // K-major: k row within the step
 #pragma unroll
@@ -192,7 +198,7 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
         src = op.p + k + src_off[i];
       else
         src = op.p + min(k + kmaj_row[i], op.k_last) * op.ld + src_off[i];
-      char* dst = smem + stage * kStageBytes + blk * 1024;
+      char* dst = smem + stage * kStage + blk * 1024;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
@@ -225,8 +231,8 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
     __builtin_amdgcn_s_setprio(0);
     wait_dma();
     lds_barrier();
-    const char* wb = smem + (kt & 1) * kStageBytes;
-    const char* hb = wb + kTileV * kBK * 2;
+    const char* wb = smem + (kt & 1) * kStage;
+    const char* hb = wb + kARows * kBK * 2;
     auto read_frags = [&](int ks, int buf) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) af[buf][a] = read_fragment<A_KMAJOR>(wb, wv * 128 + a * 32, ks);
@@ -248,7 +254,7 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
       mfma_step(1);
 #pragma unroll
       for (int q = 0; q < kBlocksPerWave; ++q) {
-        sched_group(kSchedMfma, 1);
+        if (q < 8) sched_group(kSchedMfma, 1);
         sched_group(kSchedVmemRead, 1);
       }
     } else {
