@@ -88,6 +88,26 @@ def test_logprob_only_calls_give_the_same_bits(lib, T, d, V, split):
     assert max_abs(lp, olp) <= TOL_LINEAR
 
 
+@pytest.mark.parametrize("V", [1000, 33563, 151936])
+def test_paired_tiles_match_full_tiles(lib, V):
+    """Up to 128 tokens the fused path pairs vocabulary tiles (512 x 128 workgroups); above,
+    it runs 256 x 256 tiles.  The first 128 rows of a 129-row batch, alone, must give the
+    same bits as in the batch (tiles per chunk 1, 17 (odd) and 75)."""
+    import torch
+    T, d = 129, 64
+    announce(f"linear paired vs full tiles T={T} d={d} V={V}")
+    case = S.random_fused_case(T, d, V, seed=9400 + V % 1000, h_sigma=1.0,
+                               w_sigma=3.0 / math.sqrt(d))
+    h, w, t = bits_dev(case.h_bits), bits_dev(case.w_bits), dev(case.targets)
+    lp, ent = run_linear(lib, h, w, t)
+    for split in (1, 8):
+        lps, ents = run_linear(lib, h[:128], w, t[:128], 1.0, split)
+        assert bitwise_equal(lps, lp[:128]) and bitwise_equal(ents, ent[:128]), split
+    olp, oent = oracle.linear_logprob_entropy(f32(case.h_bits), f32(case.w_bits), case.targets,
+                                              1.0)
+    assert max_abs(lp, olp) <= TOL_LINEAR and max_abs(ent, oent) <= TOL_LINEAR
+
+
 def test_token_tile_groups_with_partial_last_group(lib):
     """T = 2600: 11 token tiles, which the kernel runs as a group of 8 and a partial group
     of 3.  Every row against the oracle; the rows of the partial group alone, and vocab
