@@ -121,10 +121,15 @@ def test_qwen3_vocab_batch_and_order_bitwise(lib, cfg2):
 
 
 def test_repeats_one_distinct_result(lib, cfg2):
+    """The prior-art report's repeat check ("repeats": 10, "distinct_results_in_repeats": 1)
+    on the full workload, at vocab splits 1 and 8: twenty calls, one distinct result."""
     _, _, _, xd, td = cfg2
-    announce("logits T=1024 10 repeats")
-    outs = {run_logits(lib, xd, td)[0].tobytes() + run_logits(lib, xd, td)[1].tobytes()
-            for _ in range(5)}
+    outs = set()
+    for split in (1, 8):
+        announce(f"logits T=1024 split={split}: 10 repeats")
+        for _ in range(10):
+            lp, ent = run_logits(lib, xd, td, 1.0, split)
+            outs.add(lp.tobytes() + ent.tobytes())
     assert len(outs) == 1
 
 
