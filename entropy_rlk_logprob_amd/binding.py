@@ -6,6 +6,7 @@ fallback: if the library is missing or the device is not gfx950, calls raise.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import re
@@ -27,6 +28,7 @@ RLK_ERR_HIP = 4
 OP_FROM_LOGITS, OP_LINEAR, OP_ENTROPY, OP_COMPARE, OP_BACKWARD_FROM_LOGITS = 0, 1, 2, 3, 4
 OP_LINEAR_BACKWARD = 5
 ROW_STATE_BYTES = 24   # sizeof(rlk_row_state)
+WORKSPACE_INVALID = 2**64 - 1   # RLK_WORKSPACE_INVALID, (size_t)-1
 
 # Field order of rlk_compare_result (8 x 8 bytes: four int64, then four double).
 COMPARE_FIELDS = ("active_tokens", "mismatch_count", "bitwise_mismatch_count", "reserved",
@@ -79,17 +81,24 @@ class Library:
         import torch  # noqa: F401
         self.lib = ctypes.CDLL(path)
         L = self.lib
-        L.rlk_workspace_bytes.restype = ctypes.c_int
-        L.rlk_workspace_bytes.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, ctypes.c_int32,
-                                          ctypes.POINTER(ctypes.c_size_t)]
+        L.rlk_workspace_bytes.restype = ctypes.c_size_t
+        L.rlk_workspace_bytes.argtypes = [ctypes.c_int, _c_i64, _c_i64, _c_i64, ctypes.c_int32]
         L.rlk_logprob_from_logits.restype = ctypes.c_int
         L.rlk_logprob_from_logits.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_float,
-                                              ctypes.c_int32, _c_p, _c_p, _c_p, _c_p,
+                                              ctypes.c_int32, _c_p, _c_p, _c_p,
                                               ctypes.c_size_t, _c_p]
+        L.rlk_logprob_from_logits_with_states.restype = ctypes.c_int
+        L.rlk_logprob_from_logits_with_states.argtypes = [
+            _c_p, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_float, ctypes.c_int32, _c_p, _c_p, _c_p,
+            _c_p, ctypes.c_size_t, _c_p]
         L.rlk_linear_logprob.restype = ctypes.c_int
         L.rlk_linear_logprob.argtypes = [_c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p,
-                                         ctypes.c_float, ctypes.c_int32, _c_p, _c_p, _c_p, _c_p,
+                                         ctypes.c_float, ctypes.c_int32, _c_p, _c_p, _c_p,
                                          ctypes.c_size_t, _c_p]
+        L.rlk_linear_logprob_with_states.restype = ctypes.c_int
+        L.rlk_linear_logprob_with_states.argtypes = [
+            _c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_float,
+            ctypes.c_int32, _c_p, _c_p, _c_p, _c_p, ctypes.c_size_t, _c_p]
         L.rlk_entropy.restype = ctypes.c_int
         L.rlk_entropy.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, ctypes.c_float, ctypes.c_int32,
                                   _c_p, _c_p, ctypes.c_size_t, _c_p]
@@ -129,11 +138,12 @@ class Library:
 
     def workspace_bytes(self, op: int, n_tokens: int, vocab: int, hidden: int = 0,
                         vocab_splits: int = 1) -> int:
-        out = ctypes.c_size_t(0)
-        st = self.lib.rlk_workspace_bytes(op, n_tokens, vocab, hidden, vocab_splits,
-                                          ctypes.byref(out))
-        self.check(st, "rlk_workspace_bytes")
-        return out.value
+        n = self.lib.rlk_workspace_bytes(op, n_tokens, vocab, hidden, vocab_splits)
+        if n == WORKSPACE_INVALID:
+            raise RlkError(RLK_ERR_INVALID_ARGUMENT,
+                           f"rlk_workspace_bytes(op={op}, n_tokens={n_tokens}, vocab={vocab}, "
+                           f"hidden={hidden}, vocab_splits={vocab_splits}): invalid request")
+        return n
 
     def logprob_from_logits_raw(self, *args) -> int:
         return self.lib.rlk_logprob_from_logits(*args)
@@ -145,18 +155,21 @@ class Library:
         return self.lib.rlk_entropy(*args)
 
     # ------------------------------------------------------------------ torch wrappers
-    @staticmethod
-    def _stream_handle(stream, device) -> int:
-        import torch
-        s = stream if stream is not None else torch.cuda.current_stream(device)
-        return int(s.cuda_stream)
+    # Every wrapper makes the tensors' GPU current and the launch stream torch's current
+    # stream while it allocates outputs and workspace (so the caching allocator orders the
+    # reuse of that memory after the library's kernels on that stream), then passes the
+    # stream's handle to the library.
 
     @staticmethod
-    def _on(device):
-        """The library launches on the current HIP device: make it the tensors' device."""
+    @contextlib.contextmanager
+    def _on(device, stream=None):
+        """Yield the stream to launch on, with `device` current and that stream current."""
         import torch
         _require(device.type == "cuda", f"tensors must be on a GPU, got {device}")
-        return torch.cuda.device(device)
+        with torch.cuda.device(device):
+            s = stream if stream is not None else torch.cuda.current_stream(device)
+            with torch.cuda.stream(s):
+                yield s
 
     @staticmethod
     def _workspace(nbytes: int, device, workspace=None):
@@ -164,6 +177,7 @@ class Library:
         if nbytes == 0:
             return None, 0
         if workspace is not None:
+            _require(workspace.is_contiguous(), "workspace must be contiguous")
             if workspace.numel() * workspace.element_size() < nbytes:
                 raise RlkError(RLK_ERR_WORKSPACE_TOO_SMALL, "workspace tensor too small")
             return workspace, workspace.numel() * workspace.element_size()
@@ -185,8 +199,34 @@ class Library:
             _require(states.data_ptr() % 8 == 0, "row_states must be 8-byte aligned")
 
     @staticmethod
+    def _check_targets(targets, T: int):
+        import torch
+        _require(targets.dtype == torch.int64 and targets.is_contiguous() and
+                 targets.dim() == 1 and targets.numel() == T,
+                 f"targets must be a contiguous int64 tensor of {T} elements")
+
+    @staticmethod
+    def _check_vec_out(t, T: int, what: str):
+        import torch
+        if t is not None:
+            _require(t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == (T,),
+                     f"{what} must be a contiguous fp32 tensor of shape ({T},)")
+
+    @staticmethod
     def _ptr(t) -> int | None:
         return None if t is None else t.data_ptr()
+
+    def _vec_outputs(self, out, T: int, dev, with_entropy: bool):
+        import torch
+        if out is None:
+            return (torch.empty(T, dtype=torch.float32, device=dev),
+                    torch.empty(T, dtype=torch.float32, device=dev) if with_entropy else None)
+        _require(isinstance(out, (tuple, list)) and len(out) == 2, "out must be (logprob, entropy)")
+        lp, ent = out
+        _require(lp is not None, "out[0] (logprob) is required")
+        self._check_vec_out(lp, T, "out[0] (logprob)")
+        self._check_vec_out(ent, T, "out[1] (entropy)")
+        return lp, ent
 
     def logprob_from_logits(self, logits, targets, temperature: float = 1.0,
                             vocab_splits: int = 1, with_entropy: bool = True, out=None,
@@ -197,29 +237,29 @@ class Library:
         import torch
         _require(logits.dtype in (torch.float32, torch.bfloat16), "logits must be fp32 or bf16")
         _require(logits.dim() == 2 and logits.stride(1) == 1, "logits must be [T, V], unit stride")
-        _require(targets.dtype == torch.int64 and targets.is_contiguous(),
-                 "targets must be contiguous int64")
         T, V = logits.shape
         dev = logits.device
-        lp, ent = out if out is not None else (
-            torch.empty(T, dtype=torch.float32, device=dev),
-            torch.empty(T, dtype=torch.float32, device=dev) if with_entropy else None)
+        self._check_targets(targets, T)
+        lp, ent = (None, None) if out is None else self._vec_outputs(out, T, dev, with_entropy)
         _same_device(dev, targets, lp, ent, row_states, workspace)
-        with self._on(dev):
+        self._check_states(row_states, T)
+        _require(row_states is None or logits.dtype == torch.float32,
+                 "row states are saved by the fp32 logits call only")
+        with self._on(dev, stream) as s:
+            if out is None:
+                lp, ent = self._vec_outputs(None, T, dev, with_entropy)
             ws, wsb = self._workspace(self.workspace_bytes(OP_FROM_LOGITS, T, V, 0, vocab_splits),
                                       dev, workspace)
-            if logits.dtype == torch.float32:
-                self._check_states(row_states, T)
-                st = self.lib.rlk_logprob_from_logits(
-                    self._ptr(logits), logits.stride(0), T, V, self._ptr(targets), temperature,
-                    vocab_splits, self._ptr(lp), self._ptr(ent), self._ptr(row_states),
-                    self._ptr(ws), wsb, self._stream_handle(stream, dev))
+            args = (self._ptr(logits), logits.stride(0), T, V, self._ptr(targets), temperature,
+                    vocab_splits, self._ptr(lp), self._ptr(ent))
+            tail = (self._ptr(ws), wsb, s.cuda_stream)
+            if logits.dtype == torch.bfloat16:
+                st = self.lib.rlk_logprob_from_logits_bf16(*args, *tail)
+            elif row_states is None:
+                st = self.lib.rlk_logprob_from_logits(*args, *tail)
             else:
-                _require(row_states is None, "row states are saved by the fp32 logits call only")
-                st = self.lib.rlk_logprob_from_logits_bf16(
-                    self._ptr(logits), logits.stride(0), T, V, self._ptr(targets), temperature,
-                    vocab_splits, self._ptr(lp), self._ptr(ent), self._ptr(ws), wsb,
-                    self._stream_handle(stream, dev))
+                st = self.lib.rlk_logprob_from_logits_with_states(*args, self._ptr(row_states),
+                                                                  *tail)
         self.check(st, "rlk_logprob_from_logits")
         return lp, ent
 
@@ -230,15 +270,16 @@ class Library:
         _require(logits.dim() == 2 and logits.stride(1) == 1, "logits must be [T, V], unit stride")
         T, V = logits.shape
         dev = logits.device
-        ent = out if out is not None else torch.empty(T, dtype=torch.float32, device=dev)
-        _same_device(dev, ent, workspace)
-        with self._on(dev):
+        self._check_vec_out(out, T, "out (entropy)")
+        _same_device(dev, out, workspace)
+        with self._on(dev, stream) as s:
+            ent = out if out is not None else torch.empty(T, dtype=torch.float32, device=dev)
             ws, wsb = self._workspace(self.workspace_bytes(OP_ENTROPY, T, V, 0, vocab_splits),
                                       dev, workspace)
             fn = (self.lib.rlk_entropy if logits.dtype == torch.float32
                   else self.lib.rlk_entropy_bf16)
             st = fn(self._ptr(logits), logits.stride(0), T, V, temperature, vocab_splits,
-                    self._ptr(ent), self._ptr(ws), wsb, self._stream_handle(stream, dev))
+                    self._ptr(ent), self._ptr(ws), wsb, s.cuda_stream)
         self.check(st, "rlk_entropy")
         return ent
 
@@ -246,33 +287,37 @@ class Library:
                        vocab_splits: int = 1, with_entropy: bool = True, out=None,
                        workspace=None, stream=None, row_states=None):
         """hidden: [T, d] bf16 (or int16/uint16 bits); weight: [V, d] same; targets [T] int64."""
-        import torch
         self._check_operands(hidden, weight)
-        _require(targets.dtype == torch.int64 and targets.is_contiguous(),
-                 "targets must be contiguous int64")
         T, d = hidden.shape
         V = weight.shape[0]
         dev = hidden.device
-        lp, ent = out if out is not None else (
-            torch.empty(T, dtype=torch.float32, device=dev),
-            torch.empty(T, dtype=torch.float32, device=dev) if with_entropy else None)
+        self._check_targets(targets, T)
+        lp, ent = (None, None) if out is None else self._vec_outputs(out, T, dev, with_entropy)
         _same_device(dev, weight, targets, lp, ent, row_states, workspace)
         self._check_states(row_states, T)
-        with self._on(dev):
+        with self._on(dev, stream) as s:
+            if out is None:
+                lp, ent = self._vec_outputs(None, T, dev, with_entropy)
             ws, wsb = self._workspace(self.workspace_bytes(OP_LINEAR, T, V, d, vocab_splits), dev,
                                       workspace)
-            st = self.lib.rlk_linear_logprob(
-                self._ptr(hidden), hidden.stride(0), self._ptr(weight), weight.stride(0), T, d,
-                V, self._ptr(targets), temperature, vocab_splits, self._ptr(lp), self._ptr(ent),
-                self._ptr(row_states), self._ptr(ws), wsb, self._stream_handle(stream, dev))
+            args = (self._ptr(hidden), hidden.stride(0), self._ptr(weight), weight.stride(0), T,
+                    d, V, self._ptr(targets), temperature, vocab_splits, self._ptr(lp),
+                    self._ptr(ent))
+            tail = (self._ptr(ws), wsb, s.cuda_stream)
+            if row_states is None:
+                st = self.lib.rlk_linear_logprob(*args, *tail)
+            else:
+                st = self.lib.rlk_linear_logprob_with_states(*args, self._ptr(row_states), *tail)
         self.check(st, "rlk_linear_logprob")
         return lp, ent
 
     @staticmethod
     def _check_operands(hidden, weight):
+        import torch
+        bits16 = (torch.bfloat16, torch.int16, torch.uint16)
         _require(hidden.dim() == 2 and weight.dim() == 2, "hidden and weight must be 2-D")
-        _require(hidden.element_size() == 2 and weight.element_size() == 2,
-                 "hidden and weight must hold bf16 (2-byte) elements")
+        _require(hidden.dtype in bits16 and weight.dtype in bits16,
+                 "hidden and weight must be bfloat16 (or int16 / uint16 holding bf16 bits)")
         _require(hidden.stride(1) == 1 and weight.stride(1) == 1,
                  "hidden and weight must have unit column stride")
         _require(hidden.shape[1] == weight.shape[1], "hidden and weight disagree on hidden_dim")
@@ -297,21 +342,23 @@ class Library:
         dev = logits.device
         self._check_row_grads(T, grad_logprob, grad_entropy)
         if targets is not None:
-            _require(targets.dtype == torch.int64 and targets.is_contiguous(),
-                     "targets must be contiguous int64")
-        grad = out if out is not None else torch.empty((T, V), dtype=torch.float32, device=dev)
-        _require(grad.dtype == torch.float32 and grad.stride(1) == 1 and
-                 tuple(grad.shape) == (T, V), "out must be fp32 [T, V] with unit column stride")
-        _same_device(dev, targets, grad_logprob, grad_entropy, grad, row_states, workspace)
+            self._check_targets(targets, T)
+        if out is not None:
+            _require(out.dtype == torch.float32 and out.dim() == 2 and out.stride(1) == 1 and
+                     tuple(out.shape) == (T, V),
+                     "out must be fp32 [T, V] with unit column stride")
+        _same_device(dev, targets, grad_logprob, grad_entropy, out, row_states, workspace)
         self._check_states(row_states, T)
-        with self._on(dev):
+        with self._on(dev, stream) as s:
+            grad = out if out is not None else torch.empty((T, V), dtype=torch.float32,
+                                                           device=dev)
             ws, wsb = self._workspace(self.workspace_bytes(OP_BACKWARD_FROM_LOGITS, T, V, 0,
                                                            vocab_splits), dev, workspace)
             st = self.lib.rlk_logprob_backward_from_logits(
                 self._ptr(logits), logits.stride(0), T, V, self._ptr(targets), temperature,
                 vocab_splits, self._ptr(grad_logprob), self._ptr(grad_entropy),
                 self._ptr(row_states), self._ptr(grad), grad.stride(0), self._ptr(ws), wsb,
-                self._stream_handle(stream, dev))
+                s.cuda_stream)
         self.check(st, "rlk_logprob_backward_from_logits")
         return grad
 
@@ -328,21 +375,19 @@ class Library:
         dev = hidden.device
         self._check_row_grads(T, grad_logprob, grad_entropy)
         if targets is not None:
-            _require(targets.dtype == torch.int64 and targets.is_contiguous(),
-                     "targets must be contiguous int64")
-        if out is not None:
-            dh, dw = out
-        else:
-            dh = torch.empty((T, d), dtype=torch.float32, device=dev) if need_hidden else None
-            dw = torch.empty((V, d), dtype=torch.float32, device=dev) if need_weight else None
+            self._check_targets(targets, T)
+        dh, dw = out if out is not None else (None, None)
         for g, shape in ((dh, (T, d)), (dw, (V, d))):
-            _require(g is None or (g.dtype == torch.float32 and tuple(g.shape) == shape and
-                                   g.stride(1) == 1),
+            _require(g is None or (g.dtype == torch.float32 and g.dim() == 2 and
+                                   tuple(g.shape) == shape and g.stride(1) == 1),
                      f"gradient outputs must be fp32 {shape} with unit column stride")
         _same_device(dev, weight, targets, grad_logprob, grad_entropy, row_states, dh, dw,
                      workspace)
         self._check_states(row_states, T)
-        with self._on(dev):
+        with self._on(dev, stream) as s:
+            if out is None:
+                dh = torch.empty((T, d), dtype=torch.float32, device=dev) if need_hidden else None
+                dw = torch.empty((V, d), dtype=torch.float32, device=dev) if need_weight else None
             ws, wsb = self._workspace(self.workspace_bytes(OP_LINEAR_BACKWARD, T, V, d,
                                                            vocab_splits), dev, workspace)
             st = self.lib.rlk_linear_logprob_backward(
@@ -351,7 +396,7 @@ class Library:
                 self._ptr(grad_entropy), self._ptr(row_states), self._ptr(dh),
                 dh.stride(0) if dh is not None else 0,
                 self._ptr(dw), dw.stride(0) if dw is not None else 0, self._ptr(ws), wsb,
-                self._stream_handle(stream, dev))
+                s.cuda_stream)
         self.check(st, "rlk_linear_logprob_backward")
         return dh, dw
 
@@ -366,24 +411,30 @@ class Library:
         if mask is not None:
             _require(mask.dtype in (torch.uint8, torch.bool) and mask.shape == train.shape and
                      mask.is_contiguous(), "mask must be a contiguous [T] bool or uint8 tensor")
+        if out is not None:
+            _require(out.numel() * out.element_size() >= 64 and out.is_contiguous() and
+                     out.data_ptr() % 8 == 0, "out must hold 64 contiguous, 8-aligned bytes")
         T = train.shape[0]
         dev = train.device
-        res = out if out is not None else torch.empty(64, dtype=torch.uint8, device=dev)
-        _require(res.numel() * res.element_size() >= 64 and res.is_contiguous(),
-                 "out must hold 64 contiguous bytes")
-        _same_device(dev, rollout, mask, res, workspace)
-        with self._on(dev):
-            wsb = self.workspace_bytes(OP_COMPARE, T, 1)
-            ws, wsb = self._workspace(wsb, dev, workspace)
+        _same_device(dev, rollout, mask, out, workspace)
+        with self._on(dev, stream) as s:
+            res = out if out is not None else torch.empty(64, dtype=torch.uint8, device=dev)
+            ws, wsb = self._workspace(self.workspace_bytes(OP_COMPARE, T, 1), dev, workspace)
             st = self.lib.rlk_logprob_compare(self._ptr(train), self._ptr(rollout),
                                               self._ptr(mask), T, self._ptr(res), self._ptr(ws),
-                                              wsb, self._stream_handle(stream, dev))
+                                              wsb, s.cuda_stream)
         self.check(st, "rlk_logprob_compare")
         return res
 
     def logprob_compare(self, train, rollout, mask=None, workspace=None, stream=None) -> dict:
-        """Comparison metrics as a dict (copies the 64-byte result to the host)."""
+        """Comparison metrics as a dict (copies the 64-byte result to the host once the
+        launch stream has written it)."""
+        import torch
         res = self.logprob_compare_async(train, rollout, mask, None, workspace, stream)
+        if stream is not None:
+            stream.synchronize()
+        else:
+            torch.cuda.current_stream(train.device).synchronize()
         return unpack_compare(bytes(res.cpu().numpy().tobytes()))
 
 

@@ -108,63 +108,119 @@ rlk_status run_logits(const float* logits_f32, const uint16_t* logits_bf16, int6
   return e == hipSuccess ? RLK_OK : RLK_ERR_HIP;
 }
 
+// Shared validation of the fused forward calls (everything but the workspace); *need gets
+// the workspace bytes the call needs.
+rlk_status validate_linear(const uint16_t* hidden_bf16, int64_t ld_hidden,
+                           const uint16_t* weight_bf16, int64_t ld_weight, int64_t n_tokens,
+                           int64_t hidden_dim, int64_t vocab, const int64_t* target_ids,
+                           float temperature, int32_t vocab_splits, const float* logprob_out,
+                           const rlk_row_state* row_states_out, size_t* need) {
+  *need = 0;
+  if (n_tokens < 0 || n_tokens > kMaxRows || vocab < 1 || vocab > kMaxVocabLinear)
+    return RLK_ERR_INVALID_ARGUMENT;
+  if (hidden_dim < 64 || hidden_dim > kMaxHidden || hidden_dim % 64 != 0)
+    return RLK_ERR_INVALID_ARGUMENT;
+  if (ld_hidden < hidden_dim || ld_weight < hidden_dim || ld_hidden % 8 != 0 ||
+      ld_weight % 8 != 0 || ld_hidden > kMaxLdLinear || ld_weight > kMaxLdLinear)
+    return RLK_ERR_INVALID_ARGUMENT;
+  if (!valid_temperature(temperature) || !valid_splits(vocab_splits))
+    return RLK_ERR_INVALID_ARGUMENT;
+  if (n_tokens == 0) return RLK_OK;
+  if (!hidden_bf16 || !weight_bf16 || !target_ids || !logprob_out)
+    return RLK_ERR_INVALID_ARGUMENT;
+  if (row_states_out && !aligned(row_states_out, 8)) return RLK_ERR_INVALID_ARGUMENT;
+  if (!aligned(hidden_bf16, 16) || !aligned(weight_bf16, 16)) return RLK_ERR_INVALID_ARGUMENT;
+  *need = rlk::linear_workspace_layout(n_tokens, vocab, vocab_splits).total;
+  return RLK_OK;
+}
+
+rlk_status run_linear(const uint16_t* hidden_bf16, int64_t ld_hidden, const uint16_t* weight_bf16,
+                      int64_t ld_weight, int64_t n_tokens, int64_t hidden_dim, int64_t vocab,
+                      const int64_t* target_ids, float temperature, int32_t vocab_splits,
+                      float* logprob_out, float* entropy_out, rlk_row_state* row_states_out,
+                      void* workspace, void* stream) {
+  rlk::LinearArgs a;
+  a.H = hidden_bf16;
+  a.W = weight_bf16;
+  a.ldh = ld_hidden;
+  a.ldw = ld_weight;
+  a.T = n_tokens;
+  a.d = hidden_dim;
+  a.V = vocab;
+  a.Vc = rlk::chunk_cols(vocab);
+  a.targets = target_ids;
+  a.beta = 1.0 / (double)temperature;
+  a.c = (float)(kLog2e / (double)temperature);
+  a.S = vocab_splits;
+  a.lp = logprob_out;
+  a.ent = entropy_out;
+  a.ws = workspace;
+  a.root = reinterpret_cast<rlk::WireState*>(row_states_out);
+  const hipError_t e = rlk::launch_linear_path(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RLK_OK : RLK_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
 
-rlk_status rlk_workspace_bytes(int op, int64_t n_tokens, int64_t vocab, int64_t hidden,
-                               int32_t vocab_splits, size_t* bytes_out) {
+size_t rlk_workspace_bytes(int op, int64_t n_tokens, int64_t vocab, int64_t hidden,
+                           int32_t vocab_splits) {
   if (op == RLK_OP_COMPARE) {
-    if (!bytes_out || n_tokens < 0 || n_tokens > kMaxCompareTokens)
-      return RLK_ERR_INVALID_ARGUMENT;
-    *bytes_out = rlk::compare_workspace_bytes(n_tokens);
-    return RLK_OK;
+    if (n_tokens < 0 || n_tokens > kMaxCompareTokens) return RLK_WORKSPACE_INVALID;
+    return rlk::compare_workspace_bytes(n_tokens);
   }
-  if (!bytes_out || n_tokens < 0 || n_tokens > kMaxRows || vocab < 1 ||
-      !valid_splits(vocab_splits))
-    return RLK_ERR_INVALID_ARGUMENT;
+  if (n_tokens < 0 || n_tokens > kMaxRows || vocab < 1 || !valid_splits(vocab_splits))
+    return RLK_WORKSPACE_INVALID;
   switch (op) {
     case RLK_OP_FROM_LOGITS:
     case RLK_OP_ENTROPY:
-      if (vocab > kMaxVocab) return RLK_ERR_INVALID_ARGUMENT;
-      *bytes_out = logits_ws_bytes(n_tokens, vocab_splits);
-      return RLK_OK;
+      if (vocab > kMaxVocab) return RLK_WORKSPACE_INVALID;
+      return logits_ws_bytes(n_tokens, vocab_splits);
     case RLK_OP_BACKWARD_FROM_LOGITS:
-      if (vocab > kMaxVocab) return RLK_ERR_INVALID_ARGUMENT;
-      *bytes_out = backward_ws_bytes(n_tokens, vocab_splits);
-      return RLK_OK;
+      if (vocab > kMaxVocab) return RLK_WORKSPACE_INVALID;
+      return backward_ws_bytes(n_tokens, vocab_splits);
     case RLK_OP_LINEAR_BACKWARD:
       if (vocab > kMaxVocabLinear || hidden < 64 || hidden > kMaxHidden || hidden % 64 != 0)
-        return RLK_ERR_INVALID_ARGUMENT;
-      *bytes_out = n_tokens == 0
-                       ? 0
-                       : rlk::linear_backward_layout(n_tokens, vocab, hidden, vocab_splits).total;
-      return RLK_OK;
+        return RLK_WORKSPACE_INVALID;
+      return n_tokens == 0
+                 ? 0
+                 : rlk::linear_backward_layout(n_tokens, vocab, hidden, vocab_splits).total;
     case RLK_OP_LINEAR:
-      if (vocab > kMaxVocabLinear || hidden < 0) return RLK_ERR_INVALID_ARGUMENT;
-      *bytes_out = n_tokens == 0 ? 0
-                                 : rlk::linear_workspace_layout(n_tokens, vocab, vocab_splits).total;
-      return RLK_OK;
+      if (vocab > kMaxVocabLinear || hidden < 0) return RLK_WORKSPACE_INVALID;
+      return n_tokens == 0 ? 0 : rlk::linear_workspace_layout(n_tokens, vocab, vocab_splits).total;
     default:
-      return RLK_ERR_INVALID_ARGUMENT;
+      return RLK_WORKSPACE_INVALID;
   }
 }
 
-rlk_status rlk_logprob_from_logits(const float* logits, int64_t ld_logits, int64_t n_tokens,
-                                   int64_t vocab, const int64_t* target_ids, float temperature,
-                                   int32_t vocab_splits, float* logprob_out, float* entropy_out,
-                                   rlk_row_state* row_states_out, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
+rlk_status rlk_logprob_from_logits_with_states(const float* logits, int64_t ld_logits,
+                                               int64_t n_tokens, int64_t vocab,
+                                               const int64_t* target_ids, float temperature,
+                                               int32_t vocab_splits, float* logprob_out,
+                                               float* entropy_out,
+                                               rlk_row_state* row_states_out, void* workspace,
+                                               size_t workspace_bytes, void* stream) {
   if (n_tokens > 0 && (!target_ids || !logprob_out)) return RLK_ERR_INVALID_ARGUMENT;
+  if (row_states_out && !aligned(row_states_out, 8)) return RLK_ERR_INVALID_ARGUMENT;
   rlk_status s = validate_logits(logits, ld_logits, n_tokens, vocab, temperature, vocab_splits,
                                  workspace, workspace_bytes);
   if (s != RLK_OK) return s;
   if (n_tokens == 0) return RLK_OK;
   s = check_device();
   if (s != RLK_OK) return s;
-  if (row_states_out && !aligned(row_states_out, 8)) return RLK_ERR_INVALID_ARGUMENT;
   return run_logits(logits, nullptr, ld_logits, n_tokens, vocab, target_ids, temperature,
                     vocab_splits, logprob_out, entropy_out, row_states_out, workspace, stream);
+}
+
+rlk_status rlk_logprob_from_logits(const float* logits, int64_t ld_logits, int64_t n_tokens,
+                                   int64_t vocab, const int64_t* target_ids, float temperature,
+                                   int32_t vocab_splits, float* logprob_out, float* entropy_out,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return rlk_logprob_from_logits_with_states(logits, ld_logits, n_tokens, vocab, target_ids,
+                                             temperature, vocab_splits, logprob_out,
+                                             entropy_out, nullptr, workspace, workspace_bytes,
+                                             stream);
 }
 
 rlk_status rlk_logprob_from_logits_bf16(const uint16_t* logits, int64_t ld_logits,
@@ -213,52 +269,39 @@ rlk_status rlk_entropy(const float* logits, int64_t ld_logits, int64_t n_tokens,
                     vocab_splits, nullptr, entropy_out, nullptr, workspace, stream);
 }
 
+rlk_status rlk_linear_logprob_with_states(const uint16_t* hidden_bf16, int64_t ld_hidden,
+                                          const uint16_t* weight_bf16, int64_t ld_weight,
+                                          int64_t n_tokens, int64_t hidden_dim, int64_t vocab,
+                                          const int64_t* target_ids, float temperature,
+                                          int32_t vocab_splits, float* logprob_out,
+                                          float* entropy_out, rlk_row_state* row_states_out,
+                                          void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  size_t need = 0;
+  rlk_status s = validate_linear(hidden_bf16, ld_hidden, weight_bf16, ld_weight, n_tokens,
+                                 hidden_dim, vocab, target_ids, temperature, vocab_splits,
+                                 logprob_out, row_states_out, &need);
+  if (s != RLK_OK) return s;
+  if (n_tokens == 0) return RLK_OK;
+  if (workspace && !aligned(workspace, 256)) return RLK_ERR_INVALID_ARGUMENT;
+  if (!workspace || workspace_bytes < need) return RLK_ERR_WORKSPACE_TOO_SMALL;
+  s = check_device();
+  if (s != RLK_OK) return s;
+  return run_linear(hidden_bf16, ld_hidden, weight_bf16, ld_weight, n_tokens, hidden_dim, vocab,
+                    target_ids, temperature, vocab_splits, logprob_out, entropy_out,
+                    row_states_out, workspace, stream);
+}
+
 rlk_status rlk_linear_logprob(const uint16_t* hidden_bf16, int64_t ld_hidden,
                               const uint16_t* weight_bf16, int64_t ld_weight, int64_t n_tokens,
                               int64_t hidden_dim, int64_t vocab, const int64_t* target_ids,
                               float temperature, int32_t vocab_splits, float* logprob_out,
-                              float* entropy_out, rlk_row_state* row_states_out,
-                              void* workspace, size_t workspace_bytes, void* stream) {
-  if (n_tokens < 0 || n_tokens > kMaxRows || vocab < 1 || vocab > kMaxVocabLinear)
-    return RLK_ERR_INVALID_ARGUMENT;
-  if (hidden_dim < 64 || hidden_dim > kMaxHidden || hidden_dim % 64 != 0)
-    return RLK_ERR_INVALID_ARGUMENT;
-  if (ld_hidden < hidden_dim || ld_weight < hidden_dim || ld_hidden % 8 != 0 ||
-      ld_weight % 8 != 0 || ld_hidden > kMaxLdLinear || ld_weight > kMaxLdLinear)
-    return RLK_ERR_INVALID_ARGUMENT;
-  if (!valid_temperature(temperature) || !valid_splits(vocab_splits))
-    return RLK_ERR_INVALID_ARGUMENT;
-  if (n_tokens > 0) {
-    if (!hidden_bf16 || !weight_bf16 || !target_ids || !logprob_out)
-      return RLK_ERR_INVALID_ARGUMENT;
-    if (row_states_out && !aligned(row_states_out, 8)) return RLK_ERR_INVALID_ARGUMENT;
-    if (!aligned(hidden_bf16, 16) || !aligned(weight_bf16, 16)) return RLK_ERR_INVALID_ARGUMENT;
-    const size_t need = rlk::linear_workspace_layout(n_tokens, vocab, vocab_splits).total;
-    if (workspace && !aligned(workspace, 256)) return RLK_ERR_INVALID_ARGUMENT;
-    if (!workspace || workspace_bytes < need) return RLK_ERR_WORKSPACE_TOO_SMALL;
-  }
-  if (n_tokens == 0) return RLK_OK;
-  rlk_status s = check_device();
-  if (s != RLK_OK) return s;
-  rlk::LinearArgs a;
-  a.H = hidden_bf16;
-  a.W = weight_bf16;
-  a.ldh = ld_hidden;
-  a.ldw = ld_weight;
-  a.T = n_tokens;
-  a.d = hidden_dim;
-  a.V = vocab;
-  a.Vc = rlk::chunk_cols(vocab);
-  a.targets = target_ids;
-  a.beta = 1.0 / (double)temperature;
-  a.c = (float)(kLog2e / (double)temperature);
-  a.S = vocab_splits;
-  a.lp = logprob_out;
-  a.ent = entropy_out;
-  a.ws = workspace;
-  a.root = reinterpret_cast<rlk::WireState*>(row_states_out);
-  const hipError_t e = rlk::launch_linear_path(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? RLK_OK : RLK_ERR_HIP;
+                              float* entropy_out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return rlk_linear_logprob_with_states(hidden_bf16, ld_hidden, weight_bf16, ld_weight, n_tokens,
+                                        hidden_dim, vocab, target_ids, temperature, vocab_splits,
+                                        logprob_out, entropy_out, nullptr, workspace,
+                                        workspace_bytes, stream);
 }
 
 const char* rlk_status_string(rlk_status status) {
@@ -377,9 +420,16 @@ rlk_status rlk_linear_logprob_backward(const uint16_t* hidden_bf16, int64_t ld_h
     if (workspace && !aligned(workspace, 256)) return RLK_ERR_INVALID_ARGUMENT;
     if (!workspace || workspace_bytes < need) return RLK_ERR_WORKSPACE_TOO_SMALL;
   }
-  if (n_tokens == 0 || (!grad_hidden && !grad_weight)) return RLK_OK;
+  if (!grad_hidden && !grad_weight) return RLK_OK;
   rlk_status s = check_device();
   if (s != RLK_OK) return s;
+  if (n_tokens == 0) {
+    // The gradient of an empty sum: grad_weight is all zeros (grad_hidden has no rows).
+    if (!grad_weight) return RLK_OK;
+    const hipError_t e = rlk::launch_zero_f32(grad_weight, ld_grad_weight, vocab, hidden_dim,
+                                              static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? RLK_OK : RLK_ERR_HIP;
+  }
   rlk::LinearArgs a;
   a.H = hidden_bf16;
   a.W = weight_bf16;

@@ -115,6 +115,9 @@ hipError_t launch_linear_backward(const LinearArgs& a, const float* g_lp, const 
                                   float* dH, int64_t ld_dh, float* dW, int64_t ld_dw,
                                   const WireState* states, hipStream_t stream);
 
+// p[r * ld + c] = 0 for r < rows, c < cols (fp32); the weight gradient of an empty batch.
+hipError_t launch_zero_f32(float* p, int64_t ld, int64_t rows, int64_t cols, hipStream_t stream);
+
 // Train-vs-rollout comparison (rlk_compare.hip).
 using CompareResult = rlk_compare_result;
 int64_t compare_blocks(int64_t T);

@@ -24,6 +24,8 @@
 // not change the accumulation order), so dH is batch-invariant like the forward; dW sums
 // over the batch in increasing token order.
 
+#include <algorithm>
+
 #include "rlk_launch.hpp"
 #include "rlk_mma_tile.hpp"
 #include "rlk_state.hpp"
@@ -228,6 +230,15 @@ __global__ __launch_bounds__(256) void zero_cols_kernel(uint16_t* __restrict__ p
     p[(i / width) * ld + c_begin + i % width] = 0;
 }
 
+// Zero an fp32 matrix [rows, cols] with row stride ld (the weight gradient of an empty
+// batch).
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, int64_t ld,
+                                                       int64_t rows, int64_t cols) {
+  const int64_t n = rows * cols;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[(i / cols) * ld + i % cols] = 0.0f;
+}
+
 // Steps 4 and 5: C(m, n) = sum_k A[m, k] B[n, k] over the split's K range, in 256 x 256
 // tiles on the shared MFMA loop.  An operand is K-contiguous ([rows, K], row r at
 // X + r ld) or K-major ([K, rows], k row at X + k ld; its k rows beyond k_last are
@@ -332,6 +343,16 @@ LinearBackwardWorkspace linear_backward_layout(int64_t T, int64_t V, int64_t d, 
   off += align256((size_t)kDhSplits * (size_t)T * (size_t)d * sizeof(float));
   L.total = off;
   return L;
+}
+
+hipError_t launch_zero_f32(float* p, int64_t ld, int64_t rows, int64_t cols,
+                           hipStream_t stream) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  const int64_t n = rows * cols;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
+  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, ld, rows,
+                     cols);
+  return hipGetLastError();
 }
 
 hipError_t launch_linear_backward(const LinearArgs& fwd, const float* g_lp, const float* g_ent,

@@ -34,7 +34,8 @@
  *     so it can be captured into a HIP graph and replayed;
  *   - arguments are validated on the host before anything is launched; on error
  *     nothing is launched and no output is written;
- *   - n_tokens == 0 returns RLK_OK and launches nothing;
+ *   - n_tokens == 0 returns RLK_OK and launches nothing (two exceptions, which still
+ *     write their defined result: rlk_logprob_compare and rlk_linear_logprob_backward);
  *   - a target id outside [0, vocab) gives a NaN logprob for that row (its entropy is
  *     still computed); a NaN or +inf logit anywhere in a row, or a row whose logits are
  *     all -inf, gives NaN for both outputs of that row; -inf logits are tokens of
@@ -85,36 +86,65 @@ typedef struct {
   double u;
 } rlk_row_state;
 
-/*
- * Device workspace, in bytes, that the call `op` needs for these sizes.  Pure host
- * arithmetic (no device access).  `hidden` is ignored unless op is RLK_OP_LINEAR or
- * RLK_OP_LINEAR_BACKWARD; for RLK_OP_COMPARE only n_tokens is used (vocab, hidden,
- * vocab_splits are ignored).
- * The workspace must be 256-byte aligned; its contents on entry do not matter.
- * Returns RLK_ERR_INVALID_ARGUMENT for a bad op, negative sizes or a bad split count.
- */
-rlk_status rlk_workspace_bytes(int op, int64_t n_tokens, int64_t vocab, int64_t hidden,
-                               int32_t vocab_splits, size_t* bytes_out);
+/* rlk_workspace_bytes's answer for a request it cannot size (bad op code, negative or
+   oversized sizes, vocab_splits not in {1,2,4,8}): no allocation can satisfy it. */
+#define RLK_WORKSPACE_INVALID ((size_t)-1)
 
 /*
- * Selected-token logprob (and optionally entropy) from precomputed fp32 logits.
+ * Device workspace, in bytes, that the call `op` needs for these sizes.  Pure host
+ * arithmetic (no device access, no allocation).  `hidden` is ignored unless op is
+ * RLK_OP_LINEAR or RLK_OP_LINEAR_BACKWARD; for RLK_OP_COMPARE only n_tokens is used.
+ * The workspace itself belongs to the caller, must be 256-byte aligned, and its contents
+ * on entry do not matter.  Returns RLK_WORKSPACE_INVALID for a request no call accepts.
+ * What needs the space: the vocab-split exchange of the RL-Kernel Qwen3-Next logprob
+ * prior-art report's tp4_equals_tp1 check (each shard's partial state, merged in a fixed
+ * order, S x 24 bytes per row), the fused path's per-tile states (24 bytes per row and
+ * 256-column vocabulary tile), and the backward's saved rows and logit gradients.
+ */
+size_t rlk_workspace_bytes(int op, int64_t n_tokens, int64_t vocab, int64_t hidden,
+                           int32_t vocab_splits);
+
+/*
+ * Selected-token logprob (and optionally entropy) from precomputed fp32 logits: the
+ * "selected logprob" of each response row that the RL-Kernel issue #342 runbook compares
+ * between training and rollout (section 2, strict R/R step), scored in the RL-Kernel
+ * Qwen3-Next logprob prior-art report against the same shared logits in fp64
+ * (reference "shared_logits_fp64"), with the report's tp4_equals_tp1, batch_bitwise and
+ * distinct_results_in_repeats properties.
  *   logits        [n_tokens, ld_logits] fp32, first `vocab` columns used, ld_logits >= vocab
  *   target_ids    [n_tokens] int64
- *   temperature   finite, > 0 (the softmax is of logits / temperature)
+ *   temperature   finite, > 0 (the softmax is of logits / temperature; the h100-pcp.json
+ *                 evidence page's rollout runs at temperature .7)
  *   vocab_splits  1, 2, 4 or 8: number of contiguous vocabulary shards reduced separately
  *                 and merged (the result bits do not depend on it)
  *   logprob_out   [n_tokens] fp32
  *   entropy_out   [n_tokens] fp32, may be NULL
- *   row_states_out  [n_tokens] rlk_row_state, may be NULL: the states the backward call
- *                 can reuse instead of recomputing them
  *   workspace     rlk_workspace_bytes(RLK_OP_FROM_LOGITS, ...) bytes (may be NULL if 0)
  * Sizes: 1 <= vocab < 2^31, 0 <= n_tokens < 2^31.
+ * Errors: RLK_ERR_INVALID_ARGUMENT (null pointer where one is required, sizes, stride,
+ * temperature, split count, misaligned workspace), RLK_ERR_WORKSPACE_TOO_SMALL,
+ * RLK_ERR_UNSUPPORTED_DEVICE, RLK_ERR_HIP (a launch failed); on error no output is written.
  */
 rlk_status rlk_logprob_from_logits(const float* logits, int64_t ld_logits, int64_t n_tokens,
                                    int64_t vocab, const int64_t* target_ids, float temperature,
                                    int32_t vocab_splits, float* logprob_out, float* entropy_out,
-                                   rlk_row_state* row_states_out, void* workspace,
-                                   size_t workspace_bytes, void* stream);
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rlk_logprob_from_logits that also saves each row's reduction state for the backward
+ * calls (the analogue of saving the log-sum-exp for training, whose records on the
+ * h100-pcp.json evidence page consume the logprob and the entropy): outputs and their
+ * bits are those of rlk_logprob_from_logits.
+ *   row_states_out  [n_tokens] rlk_row_state, 8-byte aligned, may be NULL
+ * Other arguments, sizes and errors as rlk_logprob_from_logits.
+ */
+rlk_status rlk_logprob_from_logits_with_states(const float* logits, int64_t ld_logits,
+                                               int64_t n_tokens, int64_t vocab,
+                                               const int64_t* target_ids, float temperature,
+                                               int32_t vocab_splits, float* logprob_out,
+                                               float* entropy_out,
+                                               rlk_row_state* row_states_out, void* workspace,
+                                               size_t workspace_bytes, void* stream);
 
 /*
  * The same two calls on bf16 logits (16-bit patterns, [n_tokens, ld_logits] row-major):
@@ -137,7 +167,10 @@ rlk_status rlk_entropy_bf16(const uint16_t* logits, int64_t ld_logits, int64_t n
                             void* stream);
 
 /*
- * LM-head projection fused with the selected-token logprob ("linear-logp"):
+ * LM-head projection fused with the selected-token logprob ("linear-logp"): the operator
+ * whose backend id "rlkernel.linear_logp.bitwise.v1" the RL-Kernel h100-pcp.json evidence
+ * page's runtime readbacks record for both training and rollout, and whose strict symbols
+ * the RL-Kernel issue #342 runbook's preflight requires (section 1).
  * logits = hidden * weight^T are formed tile by tile in fp32 (bf16 x bf16 products,
  * fp32 accumulation in a fixed order over the hidden dimension, no split over it) and
  * never written to memory.
@@ -146,20 +179,39 @@ rlk_status rlk_entropy_bf16(const uint16_t* logits, int64_t ld_logits, int64_t n
  *   hidden_dim    a positive multiple of 64, at most 2^20; ld_hidden, ld_weight >=
  *                 hidden_dim, multiples of 8 and at most 2^22; both base pointers
  *                 16-byte aligned; vocab at most 2^26
- *   other arguments as rlk_logprob_from_logits; entropy_out and row_states_out may be NULL
- *                 (with both NULL the tiles skip the entropy terms: the logprob bits are the
- *                 same as with them)
+ *   other arguments as rlk_logprob_from_logits; entropy_out may be NULL (the tiles then
+ *                 skip the entropy terms: the logprob bits are the same as with them)
+ *   workspace     rlk_workspace_bytes(RLK_OP_LINEAR, n_tokens, vocab, hidden_dim, splits)
+ * Errors as rlk_logprob_from_logits.
  */
 rlk_status rlk_linear_logprob(const uint16_t* hidden_bf16, int64_t ld_hidden,
                               const uint16_t* weight_bf16, int64_t ld_weight, int64_t n_tokens,
                               int64_t hidden_dim, int64_t vocab, const int64_t* target_ids,
                               float temperature, int32_t vocab_splits, float* logprob_out,
-                              float* entropy_out, rlk_row_state* row_states_out,
-                              void* workspace, size_t workspace_bytes, void* stream);
+                              float* entropy_out, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /*
- * Per-token entropy only (no targets).  Bitwise equal to the entropy output of
- * rlk_logprob_from_logits with the same logits, temperature and any split count.
+ * rlk_linear_logprob that also saves each token's reduction state for
+ * rlk_linear_logprob_backward (as rlk_logprob_from_logits_with_states does for the logits
+ * path); outputs and their bits are those of rlk_linear_logprob.
+ *   row_states_out  [n_tokens] rlk_row_state, 8-byte aligned, may be NULL
+ */
+rlk_status rlk_linear_logprob_with_states(const uint16_t* hidden_bf16, int64_t ld_hidden,
+                                          const uint16_t* weight_bf16, int64_t ld_weight,
+                                          int64_t n_tokens, int64_t hidden_dim, int64_t vocab,
+                                          const int64_t* target_ids, float temperature,
+                                          int32_t vocab_splits, float* logprob_out,
+                                          float* entropy_out, rlk_row_state* row_states_out,
+                                          void* workspace, size_t workspace_bytes,
+                                          void* stream);
+
+/*
+ * Per-token entropy only (no targets): the per-token Shannon entropy (nats) of the
+ * tempered full-vocabulary softmax, the quantity behind the h100-pcp.json evidence page's
+ * train/entropy_loss records (the mean over tokens is the caller's).  Bitwise equal to the
+ * entropy output of rlk_logprob_from_logits with the same logits, temperature and any
+ * split count.  Arguments, workspace (RLK_OP_ENTROPY) and errors as rlk_logprob_from_logits.
  */
 rlk_status rlk_entropy(const float* logits, int64_t ld_logits, int64_t n_tokens, int64_t vocab,
                        float temperature, int32_t vocab_splits, float* entropy_out,
@@ -221,6 +273,8 @@ rlk_status rlk_logprob_backward_from_logits(const float* logits, int64_t ld_logi
  * The logit gradient is formed in fp32 and rounded to bf16 for the two bf16 MFMA products
  * (fp32 accumulation).  Row rules as for rlk_logprob_backward_from_logits; a NaN row of the
  * logit gradient makes the corresponding grad_hidden row, and every grad_weight entry, NaN.
+ * With n_tokens == 0 the gradient is that of an empty sum: grad_weight, when non-NULL, is
+ * filled with zeros (one small launch; no workspace is needed).
  */
 rlk_status rlk_linear_logprob_backward(const uint16_t* hidden_bf16, int64_t ld_hidden,
                                        const uint16_t* weight_bf16, int64_t ld_weight,
@@ -275,10 +329,14 @@ rlk_status rlk_logprob_compare(const float* train_logprob, const float* rollout_
                                rlk_compare_result* result, void* workspace,
                                size_t workspace_bytes, void* stream);
 
-/* Static, NUL-terminated description of a status code. */
+/* Static, NUL-terminated description of a status code (never NULL; "unknown status" for a
+   value outside the enum).  The runbook's preflight (issue #342, section 1) fails closed
+   with a reason instead of falling back; this is the reason's text. */
 const char* rlk_status_string(rlk_status status);
 
-/* Static identifier of the implementation that runs (recorded next to results). */
+/* Static identifier of the implementation that runs, "rlk.logprob.strict.gfx950.v1",
+   recorded next to results as the h100-pcp.json evidence page's runtime readbacks record
+   each operator's backend id (e.g. "rlkernel.linear_logp.bitwise.v1") with no fallback. */
 const char* rlk_backend_id(void);
 
 #ifdef __cplusplus

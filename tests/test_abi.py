@@ -34,6 +34,8 @@ def test_exports_every_header_symbol(L):
     names = B.header_functions()
     assert set(names) == {"rlk_workspace_bytes", "rlk_logprob_from_logits", "rlk_linear_logprob",
                           "rlk_entropy", "rlk_status_string", "rlk_backend_id",
+                          "rlk_logprob_from_logits_with_states",
+                          "rlk_linear_logprob_with_states",
                           "rlk_logprob_from_logits_bf16", "rlk_entropy_bf16",
                           "rlk_logprob_compare", "rlk_logprob_backward_from_logits",
                           "rlk_linear_logprob_backward"}
@@ -76,18 +78,40 @@ def test_workspace_sizes(L):
     lin4 = L.workspace_bytes(B.OP_LINEAR, 1024, 151936, 2048, 4)
     assert lin4 == lin + 4 * 1024 * 24
     assert L.workspace_bytes(B.OP_LINEAR, 0, 151936, 2048, 1) == 0
-    out = ctypes.c_size_t()
-    assert L.lib.rlk_workspace_bytes(7, 1, 1, 0, 1, ctypes.byref(out)) == B.RLK_ERR_INVALID_ARGUMENT
-    assert L.lib.rlk_workspace_bytes(0, 1, 1, 0, 3, ctypes.byref(out)) == B.RLK_ERR_INVALID_ARGUMENT
-    assert L.lib.rlk_workspace_bytes(0, -1, 1, 0, 1, ctypes.byref(out)) == B.RLK_ERR_INVALID_ARGUMENT
-    assert L.lib.rlk_workspace_bytes(0, 1, 0, 0, 1, ctypes.byref(out)) == B.RLK_ERR_INVALID_ARGUMENT
-    assert L.lib.rlk_workspace_bytes(0, 1, 1, 0, 1, None) == B.RLK_ERR_INVALID_ARGUMENT
+    bad = B.WORKSPACE_INVALID
+    assert L.lib.rlk_workspace_bytes(7, 1, 1, 0, 1) == bad          # op code
+    assert L.lib.rlk_workspace_bytes(0, 1, 1, 0, 3) == bad          # split count
+    assert L.lib.rlk_workspace_bytes(0, -1, 1, 0, 1) == bad         # negative n_tokens
+    assert L.lib.rlk_workspace_bytes(0, 1, 0, 0, 1) == bad          # empty vocabulary
+    assert L.lib.rlk_workspace_bytes(1, 1, (1 << 26) + 1, 64, 1) == bad  # fused vocabulary
+    assert L.lib.rlk_workspace_bytes(3, -1, 0, 0, 0) == bad         # compare: negative
+    with pytest.raises(B.RlkError):
+        L.workspace_bytes(B.OP_FROM_LOGITS, 1, 1, 0, 3)
 
 
 def call_logits(L, logits=FAKE, ld=1024, T=4, V=1024, targets=FAKE, tau=1.0, S=1, lp=FAKE,
                 ent=FAKE, ws=None, wsb=0):
-    return L.logprob_from_logits_raw(logits, ld, T, V, targets, tau, S, lp, ent, None, ws, wsb,
-                                     None)
+    return L.logprob_from_logits_raw(logits, ld, T, V, targets, tau, S, lp, ent, ws, wsb, None)
+
+
+def test_with_states_variants_validate_like_the_plain_calls(L):
+    """The _with_states calls take the plain call's arguments plus the row-state output;
+    a misaligned state pointer is rejected, and every plain-call error is returned alike."""
+    f = L.lib.rlk_logprob_from_logits_with_states
+    assert f(FAKE, 1024, 4, 1024, FAKE, 1.0, 1, FAKE, FAKE, FAKE + 4, None, 0, None) == \
+        B.RLK_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 1000, 4, 1024, FAKE, 1.0, 1, FAKE, FAKE, FAKE, None, 0, None) == \
+        B.RLK_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 1024, 4, 1024, FAKE, 1.0, 4, FAKE, FAKE, FAKE, None, 0, None) == \
+        B.RLK_ERR_WORKSPACE_TOO_SMALL
+    assert f(None, 1024, 0, 1024, None, 1.0, 1, None, None, None, None, 0, None) == B.RLK_OK
+    g = L.lib.rlk_linear_logprob_with_states
+    assert g(FAKE, 2048, FAKE, 2048, 4, 2048, 1000, FAKE, 1.0, 1, FAKE, None, FAKE + 4, FAKE,
+             1 << 30, None) == B.RLK_ERR_INVALID_ARGUMENT
+    assert g(FAKE, 2048, FAKE, 2048, 4, 2048, 1000, FAKE, 1.0, 1, FAKE, None, FAKE, FAKE, 100,
+             None) == B.RLK_ERR_WORKSPACE_TOO_SMALL
+    assert g(None, 2048, None, 2048, 0, 2048, 1000, None, 1.0, 1, None, None, None, None, 0,
+             None) == B.RLK_OK
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -163,8 +187,6 @@ def test_compare_workspace_and_result_layout(L):
     (dict(ws=None), B.RLK_ERR_WORKSPACE_TOO_SMALL),
     (dict(wsb=127), B.RLK_ERR_WORKSPACE_TOO_SMALL),
     (dict(ws=FAKE + 64), B.RLK_ERR_INVALID_ARGUMENT),
-    (dict(), B.RLK_ERR_UNSUPPORTED_DEVICE),                 # valid: reaches the device check
-    (dict(T=0, train=None, rollout=None, ws=None, wsb=0), B.RLK_ERR_UNSUPPORTED_DEVICE),
 ])
 def test_compare_validation(L, kw, code):
     a = dict(train=FAKE, rollout=FAKE, mask=None, T=5000, res=FAKE, ws=FAKE, wsb=128)
@@ -186,7 +208,6 @@ def test_backward_workspace(L):
     (dict(ld=1000), B.RLK_ERR_INVALID_ARGUMENT),
     (dict(ldg=1000), B.RLK_ERR_INVALID_ARGUMENT),
     (dict(targets=None), B.RLK_ERR_INVALID_ARGUMENT),            # grad_logprob without targets
-    (dict(targets=None, glp=None), B.RLK_ERR_UNSUPPORTED_DEVICE),  # entropy-only: valid
     (dict(grad=FAKE, ldg=1028), B.RLK_ERR_INVALID_ARGUMENT),       # in place with another ld
     (dict(tau=-1.0), B.RLK_ERR_INVALID_ARGUMENT),
     (dict(S=3), B.RLK_ERR_INVALID_ARGUMENT),
@@ -195,16 +216,18 @@ def test_backward_workspace(L):
     (dict(ws=FAKE + 16), B.RLK_ERR_INVALID_ARGUMENT),
     (dict(T=0, logits=None, grad=None, ws=None, wsb=0), B.RLK_OK),
     (dict(states=FAKE + 4), B.RLK_ERR_INVALID_ARGUMENT),             # misaligned row states
-    (dict(states=FAKE), B.RLK_ERR_UNSUPPORTED_DEVICE),
-    (dict(), B.RLK_ERR_UNSUPPORTED_DEVICE),
 ])
 def test_backward_validation(L, kw, code):
+    assert call_backward(L, **kw) == code
+
+
+def call_backward(L, **kw):
     a = dict(logits=FAKE, ld=1024, T=4, V=1024, targets=FAKE, tau=1.0, S=1, glp=FAKE, gent=None,
              grad=FAKE + 0x100000, ldg=1024, ws=FAKE, wsb=4 * 24)
     a.update(kw)
-    assert L.lib.rlk_logprob_backward_from_logits(
+    return L.lib.rlk_logprob_backward_from_logits(
         a["logits"], a["ld"], a["T"], a["V"], a["targets"], a["tau"], a["S"], a["glp"],
-        a["gent"], a.get("states"), a["grad"], a["ldg"], a["ws"], a["wsb"], None) == code
+        a["gent"], a.get("states"), a["grad"], a["ldg"], a["ws"], a["wsb"], None)
 
 
 def test_linear_backward_workspace_and_validation(L):
@@ -219,16 +242,7 @@ def test_linear_backward_workspace_and_validation(L):
     assert L.workspace_bytes(B.OP_LINEAR_BACKWARD, 0, V, d, 1) == 0
     with pytest.raises(B.RlkError):
         L.workspace_bytes(B.OP_LINEAR_BACKWARD, T, V, 100, 1)         # d not a multiple of 64
-    f = L.lib.rlk_linear_logprob_backward
-    base = dict(h=FAKE, ldh=2048, w=FAKE, ldw=2048, T=4, d=2048, V=1000, tg=FAKE, tau=1.0, S=1,
-                glp=FAKE, gent=None, dh=FAKE, lddh=2048, dw=FAKE, lddw=2048, ws=FAKE, wsb=1 << 40)
-
-    def call(**kw):
-        a = dict(base)
-        a.update(kw)
-        return f(a["h"], a["ldh"], a["w"], a["ldw"], a["T"], a["d"], a["V"], a["tg"], a["tau"],
-                 a["S"], a["glp"], a["gent"], a.get("states"), a["dh"], a["lddh"], a["dw"],
-                 a["lddw"], a["ws"], a["wsb"], None)
+    call = lambda **kw: call_linear_backward(L, **kw)  # noqa: E731
     assert call(d=96) == B.RLK_ERR_INVALID_ARGUMENT
     assert call(lddh=1000) == B.RLK_ERR_INVALID_ARGUMENT
     assert call(lddw=1000) == B.RLK_ERR_INVALID_ARGUMENT
@@ -237,15 +251,23 @@ def test_linear_backward_workspace_and_validation(L):
     assert call(wsb=1000) == B.RLK_ERR_WORKSPACE_TOO_SMALL
     assert call(ws=FAKE + 64) == B.RLK_ERR_INVALID_ARGUMENT
     assert call(dh=None, dw=None) == B.RLK_OK                      # nothing requested
-    assert call(T=0, h=None, w=None, ws=None, wsb=0) == B.RLK_OK
-    assert call() == B.RLK_ERR_UNSUPPORTED_DEVICE
-    assert call(tg=None, glp=None, gent=FAKE) == B.RLK_ERR_UNSUPPORTED_DEVICE
+    assert call(T=0, h=None, w=None, ws=None, wsb=0, dh=None, dw=None) == B.RLK_OK
     assert call(states=FAKE + 4) == B.RLK_ERR_INVALID_ARGUMENT
+
+
+def call_linear_backward(L, **kw):
+    a = dict(h=FAKE, ldh=2048, w=FAKE, ldw=2048, T=4, d=2048, V=1000, tg=FAKE, tau=1.0, S=1,
+             glp=FAKE, gent=None, dh=FAKE, lddh=2048, dw=FAKE, lddw=2048, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return L.lib.rlk_linear_logprob_backward(
+        a["h"], a["ldh"], a["w"], a["ldw"], a["T"], a["d"], a["V"], a["tg"], a["tau"], a["S"],
+        a["glp"], a["gent"], a.get("states"), a["dh"], a["lddh"], a["dw"], a["lddw"], a["ws"],
+        a["wsb"], None)
 
 
 def call_linear(L, h=FAKE, ldh=2048, w=FAKE, ldw=2048, T=4, d=2048, V=1000, tg=FAKE, tau=1.0,
                 S=1, lp=FAKE, ent=None, ws=FAKE, wsb=1 << 30):
-    return L.linear_logprob_raw(h, ldh, w, ldw, T, d, V, tg, tau, S, lp, ent, None, ws, wsb, None)
+    return L.linear_logprob_raw(h, ldh, w, ldw, T, d, V, tg, tau, S, lp, ent, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -273,6 +295,19 @@ def test_linear_validation(L, kw, code):
 
 @pytest.mark.skipif(not no_gpu_visible(), reason="would launch on placeholder pointers")
 def test_valid_call_without_gfx950_is_unsupported_device(L):
+    """Arguments that pass validation reach the device check (run only where no GPU is
+    visible: on a GPU these calls would launch on the placeholder pointers)."""
+    cmp = L.lib.rlk_logprob_compare
+    assert cmp(FAKE, FAKE, None, 5000, FAKE, FAKE, 128, None) == B.RLK_ERR_UNSUPPORTED_DEVICE
+    assert cmp(None, None, None, 0, FAKE, None, 0, None) == B.RLK_ERR_UNSUPPORTED_DEVICE
+    assert call_backward(L, targets=None, glp=None) == B.RLK_ERR_UNSUPPORTED_DEVICE
+    assert call_backward(L, states=FAKE) == B.RLK_ERR_UNSUPPORTED_DEVICE
+    assert call_backward(L) == B.RLK_ERR_UNSUPPORTED_DEVICE
+    assert call_linear_backward(L) == B.RLK_ERR_UNSUPPORTED_DEVICE
+    assert call_linear_backward(L, tg=None, glp=None, gent=FAKE) == B.RLK_ERR_UNSUPPORTED_DEVICE
+    # an empty batch still writes its zero weight gradient
+    assert call_linear_backward(L, T=0, h=None, w=None, ws=None, wsb=0) == \
+        B.RLK_ERR_UNSUPPORTED_DEVICE
     assert call_logits(L) == B.RLK_ERR_UNSUPPORTED_DEVICE
     assert call_linear(L) == B.RLK_ERR_UNSUPPORTED_DEVICE
     assert L.entropy_raw(FAKE, 1024, 4, 1024, 1.0, 1, FAKE, None, 0, None) == \

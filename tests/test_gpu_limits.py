@@ -64,3 +64,12 @@ def test_backward_calls_with_no_tokens(lib):
     dh, dw = lib.linear_logprob_backward(h, w, t, 1.0, 1, torch.empty(0, device="cuda"), None)
     torch.cuda.synchronize()
     assert g.numel() == 0 and dh.numel() == 0 and dw.shape == (10, 64)
+    # the weight gradient of an empty batch is zero, also into a strided caller buffer whose
+    # padding columns must stay untouched
+    assert torch.equal(dw, torch.zeros_like(dw))
+    buf = torch.full((10, 72), 7.0, device="cuda")
+    lib.linear_logprob_backward(h, w, t, 1.0, 1, None, None, need_hidden=False,
+                                out=(None, buf[:, :64]))
+    torch.cuda.synchronize()
+    assert torch.equal(buf[:, :64], torch.zeros(10, 64, device="cuda"))
+    assert torch.equal(buf[:, 64:], torch.full((10, 8), 7.0, device="cuda"))
