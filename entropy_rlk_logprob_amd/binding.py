@@ -29,6 +29,7 @@ OP_FROM_LOGITS, OP_LINEAR, OP_ENTROPY, OP_COMPARE, OP_BACKWARD_FROM_LOGITS = 0, 
 OP_LINEAR_BACKWARD = 5
 ROW_STATE_BYTES = 24   # sizeof(rlk_row_state)
 WORKSPACE_INVALID = 2**64 - 1   # RLK_WORKSPACE_INVALID, (size_t)-1
+NOALLOC_SCRATCH_BYTES = 64 << 20  # RLK_NOALLOC_SCRATCH_BYTES
 
 # Field order of rlk_compare_result (8 x 8 bytes: four int64, then four double).
 COMPARE_FIELDS = ("active_tokens", "mismatch_count", "bitwise_mismatch_count", "reserved",
@@ -99,6 +100,10 @@ class Library:
         L.rlk_linear_logprob_with_states.argtypes = [
             _c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_float,
             ctypes.c_int32, _c_p, _c_p, _c_p, _c_p, ctypes.c_size_t, _c_p]
+        L.rlk_linear_logprob_noalloc.restype = ctypes.c_int
+        L.rlk_linear_logprob_noalloc.argtypes = [
+            _c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, ctypes.c_float,
+            ctypes.c_int32, _c_p, _c_p, _c_p]
         L.rlk_entropy.restype = ctypes.c_int
         L.rlk_entropy.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, ctypes.c_float, ctypes.c_int32,
                                   _c_p, _c_p, ctypes.c_size_t, _c_p]
@@ -309,6 +314,30 @@ class Library:
             else:
                 st = self.lib.rlk_linear_logprob_with_states(*args, self._ptr(row_states), *tail)
         self.check(st, "rlk_linear_logprob")
+        return lp, ent
+
+    def linear_logprob_noalloc(self, hidden, weight, targets, temperature: float = 1.0,
+                               vocab_splits: int = 1, with_entropy: bool = True, out=None,
+                               stream=None):
+        """rlk_linear_logprob_noalloc: the fused call on the library's static device scratch
+        (no workspace; the library allocates nothing).  Outputs are allocated here unless
+        `out` is given.  Calls that overlap on one GPU share its scratch and must not run
+        concurrently."""
+        self._check_operands(hidden, weight)
+        T, d = hidden.shape
+        V = weight.shape[0]
+        dev = hidden.device
+        self._check_targets(targets, T)
+        lp, ent = (None, None) if out is None else self._vec_outputs(out, T, dev, with_entropy)
+        _same_device(dev, weight, targets, lp, ent)
+        with self._on(dev, stream) as s:
+            if out is None:
+                lp, ent = self._vec_outputs(None, T, dev, with_entropy)
+            st = self.lib.rlk_linear_logprob_noalloc(
+                self._ptr(hidden), hidden.stride(0), self._ptr(weight), weight.stride(0), T, d,
+                V, self._ptr(targets), temperature, vocab_splits, self._ptr(lp), self._ptr(ent),
+                s.cuda_stream)
+        self.check(st, "rlk_linear_logprob_noalloc")
         return lp, ent
 
     @staticmethod

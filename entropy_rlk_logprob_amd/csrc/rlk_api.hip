@@ -160,6 +160,31 @@ rlk_status run_linear(const uint16_t* hidden_bf16, int64_t ld_hidden, const uint
   return e == hipSuccess ? RLK_OK : RLK_ERR_HIP;
 }
 
+// Workspace of rlk_linear_logprob_noalloc: one static device array, which every GPU the
+// library runs on holds (its own copy) until the process ends.  Host code never uses the
+// array's name as an address (it is a host-side stand-in there): each device's address comes
+// from hipGetSymbolAddress, taken once per device with that device current.  The fused
+// forward writes every byte of the workspace it reads, so nothing needs clearing between
+// calls.
+__device__ __align__(256) unsigned char scratch[RLK_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+rlk_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return RLK_ERR_UNSUPPORTED_DEVICE;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return RLK_ERR_HIP;
+    }
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return RLK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -302,6 +327,29 @@ rlk_status rlk_linear_logprob(const uint16_t* hidden_bf16, int64_t ld_hidden,
                                         hidden_dim, vocab, target_ids, temperature, vocab_splits,
                                         logprob_out, entropy_out, nullptr, workspace,
                                         workspace_bytes, stream);
+}
+
+rlk_status rlk_linear_logprob_noalloc(const uint16_t* hidden_bf16, int64_t ld_hidden,
+                                      const uint16_t* weight_bf16, int64_t ld_weight,
+                                      int64_t n_tokens, int64_t hidden_dim, int64_t vocab,
+                                      const int64_t* target_ids, float temperature,
+                                      int32_t vocab_splits, float* logprob_out,
+                                      float* entropy_out, void* stream) {
+  size_t need = 0;
+  rlk_status s = validate_linear(hidden_bf16, ld_hidden, weight_bf16, ld_weight, n_tokens,
+                                 hidden_dim, vocab, target_ids, temperature, vocab_splits,
+                                 logprob_out, nullptr, &need);
+  if (s != RLK_OK) return s;
+  if (n_tokens == 0) return RLK_OK;
+  if (need > (size_t)RLK_NOALLOC_SCRATCH_BYTES) return RLK_ERR_WORKSPACE_TOO_SMALL;
+  s = check_device();
+  if (s != RLK_OK) return s;
+  void* ws = nullptr;
+  s = scratch_of_current_device(&ws);
+  if (s != RLK_OK) return s;
+  return run_linear(hidden_bf16, ld_hidden, weight_bf16, ld_weight, n_tokens, hidden_dim, vocab,
+                    target_ids, temperature, vocab_splits, logprob_out, entropy_out, nullptr, ws,
+                    stream);
 }
 
 const char* rlk_status_string(rlk_status status) {

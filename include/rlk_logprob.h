@@ -207,6 +207,31 @@ rlk_status rlk_linear_logprob_with_states(const uint16_t* hidden_bf16, int64_t l
                                           void* stream);
 
 /*
+ * rlk_linear_logprob for callers that cannot allocate: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  It takes no workspace argument and
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine): its workspace is
+ * one static device array of RLK_NOALLOC_SCRATCH_BYTES, which each GPU the library runs on
+ * holds from the first call on it until the process ends.  Same kernels as
+ * rlk_linear_logprob, so the outputs are bitwise those of rlk_linear_logprob.
+ *   arguments     as rlk_linear_logprob, without workspace and workspace_bytes
+ *   limit         rlk_workspace_bytes(RLK_OP_LINEAR, n_tokens, vocab, hidden_dim,
+ *                 vocab_splits) <= RLK_NOALLOC_SCRATCH_BYTES, else
+ *                 RLK_ERR_WORKSPACE_TOO_SMALL (nothing launched); at vocab 151936 that is
+ *                 up to 4659 tokens with vocab_splits 1 (24 bytes per token and 256-column
+ *                 vocabulary tile, plus the split exchange)
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU (other streams
+ * or threads) race and must be serialised by the caller.  No call needs the array cleared.
+ */
+#define RLK_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+rlk_status rlk_linear_logprob_noalloc(const uint16_t* hidden_bf16, int64_t ld_hidden,
+                                      const uint16_t* weight_bf16, int64_t ld_weight,
+                                      int64_t n_tokens, int64_t hidden_dim, int64_t vocab,
+                                      const int64_t* target_ids, float temperature,
+                                      int32_t vocab_splits, float* logprob_out,
+                                      float* entropy_out, void* stream);
+
+/*
  * Per-token entropy only (no targets): the per-token Shannon entropy (nats) of the
  * tempered full-vocabulary softmax, the quantity behind the h100-pcp.json evidence page's
  * train/entropy_loss records (the mean over tokens is the caller's).  Bitwise equal to the

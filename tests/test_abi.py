@@ -35,7 +35,7 @@ def test_exports_every_header_symbol(L):
     assert set(names) == {"rlk_workspace_bytes", "rlk_logprob_from_logits", "rlk_linear_logprob",
                           "rlk_entropy", "rlk_status_string", "rlk_backend_id",
                           "rlk_logprob_from_logits_with_states",
-                          "rlk_linear_logprob_with_states",
+                          "rlk_linear_logprob_with_states", "rlk_linear_logprob_noalloc",
                           "rlk_logprob_from_logits_bf16", "rlk_entropy_bf16",
                           "rlk_logprob_compare", "rlk_logprob_backward_from_logits",
                           "rlk_linear_logprob_backward"}
@@ -293,6 +293,28 @@ def test_linear_validation(L, kw, code):
     assert call_linear(L, **kw) == code
 
 
+def test_noalloc_validates_and_bounds_its_scratch_on_the_host(L):
+    """rlk_linear_logprob_noalloc checks its arguments as rlk_linear_logprob does, and rejects
+    a call whose workspace would not fit its static scratch before touching any device."""
+    f = L.lib.rlk_linear_logprob_noalloc
+    V, d = 151936, 2048
+    assert L.workspace_bytes(B.OP_LINEAR, 4659, V, d, 1) <= B.NOALLOC_SCRATCH_BYTES
+    assert L.workspace_bytes(B.OP_LINEAR, 4660, V, d, 1) > B.NOALLOC_SCRATCH_BYTES
+    assert f(FAKE, d, FAKE, d, 4660, d, V, FAKE, 1.0, 1, FAKE, FAKE, None) == \
+        B.RLK_ERR_WORKSPACE_TOO_SMALL
+    assert f(FAKE, d, FAKE, d, 4600, d, V, FAKE, 1.0, 8, FAKE, FAKE, None) == \
+        B.RLK_ERR_WORKSPACE_TOO_SMALL          # fits at split 1; 8 splits add 8 x 24 B per token
+    assert f(FAKE, d, FAKE, d, 4, 100, V, FAKE, 1.0, 1, FAKE, FAKE, None) == \
+        B.RLK_ERR_INVALID_ARGUMENT             # hidden_dim not a multiple of 64
+    assert f(FAKE, d, FAKE, d, 4, d, V, None, 1.0, 1, FAKE, FAKE, None) == \
+        B.RLK_ERR_INVALID_ARGUMENT             # no targets
+    assert f(FAKE, d, FAKE, d, 4, d, V, FAKE, 0.0, 1, FAKE, FAKE, None) == \
+        B.RLK_ERR_INVALID_ARGUMENT             # temperature
+    assert f(FAKE + 2, d, FAKE, d, 4, d, V, FAKE, 1.0, 1, FAKE, FAKE, None) == \
+        B.RLK_ERR_INVALID_ARGUMENT             # misaligned hidden
+    assert f(None, d, None, d, 0, d, V, None, 1.0, 1, None, None, None) == B.RLK_OK
+
+
 @pytest.mark.skipif(not no_gpu_visible(), reason="would launch on placeholder pointers")
 def test_valid_call_without_gfx950_is_unsupported_device(L):
     """Arguments that pass validation reach the device check (run only where no GPU is
@@ -310,6 +332,8 @@ def test_valid_call_without_gfx950_is_unsupported_device(L):
         B.RLK_ERR_UNSUPPORTED_DEVICE
     assert call_logits(L) == B.RLK_ERR_UNSUPPORTED_DEVICE
     assert call_linear(L) == B.RLK_ERR_UNSUPPORTED_DEVICE
+    assert L.lib.rlk_linear_logprob_noalloc(FAKE, 2048, FAKE, 2048, 4, 2048, 1000, FAKE, 1.0, 1,
+                                            FAKE, None, None) == B.RLK_ERR_UNSUPPORTED_DEVICE
     assert L.entropy_raw(FAKE, 1024, 4, 1024, 1.0, 1, FAKE, None, 0, None) == \
         B.RLK_ERR_UNSUPPORTED_DEVICE
     assert L.lib.rlk_logprob_from_logits_bf16(FAKE, 1024, 4, 1024, FAKE, 1.0, 1, FAKE, None, None,
