@@ -15,7 +15,8 @@ with 128-row responses packed 2048 tokens per GPU and rollout temperature 0.7):
          targets uniform
   cfg 4  fused,  T=2048 = 16 sequences x 128 rows, d=4096, V=151936, tau=1, targets uniform
   cfg 5  fused,  T=16384 in sequences of length uniform in {128..4096}, d=4096,
-         V=151936, tau=0.7 (targets are drawn by the tests from the tempered softmax)
+         V=151936, tau=0.7 (targets drawn from the tempered softmax by the oracle, stored
+         with the parity goldens by tests/golden/make_fused_goldens.py)
 
 Seeding: ``numpy.random.SeedSequence(1000 + cfg).spawn(5)`` gives independent streams
 for [logits or H, W, spikes, targets, permutations].
@@ -203,6 +204,18 @@ def fused_workload(cfg: int) -> FusedCase:
 def target_uniforms(cfg: int, n: int) -> np.ndarray:
     """Seeded uniforms in [0,1) for drawing targets by inverse CDF (cfg 5)."""
     return streams(cfg_seed(cfg))[STREAM_TARGET].random(n)
+
+
+def upstream_grads(cfg: int, n: int, masked_every: int = 7):
+    """Seeded per-row upstream gradients (g_logprob, g_entropy) ~ N(0, 1) fp32 for a
+    backward call on workload `cfg`; every `masked_every`-th row has both at 0 (a padding
+    row of a training batch)."""
+    rng = np.random.default_rng(np.random.SeedSequence(cfg_seed(cfg)).spawn(6)[5])
+    gl = rng.standard_normal(n, dtype=np.float32)
+    ge = rng.standard_normal(n, dtype=np.float32)
+    gl[::masked_every] = 0.0
+    ge[::masked_every] = 0.0
+    return gl, ge
 
 
 def permutations(cfg: int, n: int, k: int = 3) -> list[np.ndarray]:

@@ -4,4 +4,4 @@ from .logprob import (  # noqa: F401
     tempered_logits,
 )
 from .compare import METRIC_NAMES, logprob_compare  # noqa: F401
-from .backward import linear_grads, logits_grad  # noqa: F401
+from .backward import linear_grads, linear_grads_sampled, logits_grad  # noqa: F401

@@ -42,7 +42,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["logits_grad", "linear_grads"]
+__all__ = ["logits_grad", "linear_grads", "linear_grads_sampled"]
 
 
 def logits_grad(x: np.ndarray, targets: np.ndarray, temperature: float,
@@ -88,3 +88,41 @@ def linear_grads(h: np.ndarray, w: np.ndarray, targets: np.ndarray, temperature:
     w = np.asarray(w, dtype=np.float64)
     gx = logits_grad(h @ w.T, targets, temperature, g_lp, g_ent)
     return gx @ w, gx.T @ h
+
+
+def linear_grads_sampled(h: np.ndarray, w: np.ndarray, targets: np.ndarray, temperature: float,
+                         g_lp: np.ndarray | None, g_ent: np.ndarray | None,
+                         h_rows: np.ndarray, w_rows: np.ndarray, block: int = 512):
+    """Selected rows of the fused gradients of linear_grads, for batches whose full dW or
+    logits would not fit: dh[h_rows] [len(h_rows), d] and dW[w_rows] [len(w_rows), d],
+    together with the magnitudes sum |grad| |W| (for the dh rows) and sum |grad| |h| (for
+    the dW rows) that bound the rounding of these products.
+
+    The same chain rule over row blocks: a block's logits x = h_b W^T (float64), its
+    gradient g = logits_grad(x, ...); dh of a selected row is its g row times W, and dW of a
+    selected vocabulary row v is the sum over the blocks of g[:, v]^T h_b."""
+    h = np.asarray(h, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    T = h.shape[0]
+    h_rows = np.asarray(h_rows, dtype=np.int64)
+    w_rows = np.asarray(w_rows, dtype=np.int64)
+    gl = None if g_lp is None else np.asarray(g_lp)
+    ge = None if g_ent is None else np.asarray(g_ent)
+    dh = np.zeros((len(h_rows), h.shape[1]))
+    dh_mag = np.zeros_like(dh)
+    dw = np.zeros((len(w_rows), h.shape[1]))
+    dw_mag = np.zeros_like(dw)
+    w_abs = np.abs(w)
+    for r0 in range(0, T, block):
+        r1 = min(T, r0 + block)
+        g = logits_grad(h[r0:r1] @ w.T, np.asarray(targets)[r0:r1], temperature,
+                        None if gl is None else gl[r0:r1], None if ge is None else ge[r0:r1])
+        sel = np.flatnonzero((h_rows >= r0) & (h_rows < r1))
+        if sel.size:
+            gs = g[h_rows[sel] - r0]
+            dh[sel] = gs @ w
+            dh_mag[sel] = np.abs(gs) @ w_abs
+        gv = g[:, w_rows]
+        dw += gv.T @ h[r0:r1]
+        dw_mag += np.abs(gv).T @ np.abs(h[r0:r1])
+    return dh, dw, dh_mag, dw_mag

@@ -18,8 +18,14 @@ report (pr549, report.json) is "shared_logits_fp64" over all 1024 tokens of the 
 is that reference for the fused workloads: every row, logits as exact float64 dot products
 of the bf16 values.
 
-Usage:  python tests/golden/make_fused_goldens.py [--rows-per-block 512] [--only NAME]
-About 5 minutes on 8 cores (20 TFLOP of float64 matrix products for the largest workload).
+For the T=16384 workload it also stores selected rows of the fused backward's gradients
+(dH for 48 tokens, dW for 48 vocabulary rows, oracle.linear_grads_sampled) under seeded
+upstream gradients, with the magnitudes that bound their rounding.
+
+Usage:  python tests/golden/make_fused_goldens.py [--rows-per-block 512] [--only CFG]
+                                                  [--backward-only]
+About 10 minutes on 8 cores (the largest workload's float64 logits, 20 TFLOP, are formed
+twice: for the forward values and for the backward rows).
 """
 from __future__ import annotations
 
@@ -97,10 +103,49 @@ def make(cfg: int, rows_per_block: int) -> dict:
     }
 
 
+def sampled_rows(T: int, V: int, targets: np.ndarray, seed: int = 77):
+    """The token rows (of dH) and vocabulary rows (of dW) the backward goldens store: the
+    ends, rows around the backward's token-chunk boundaries (multiples of 2048) and the
+    canonical vocabulary chunks' boundaries, a few targets, and seeded random rows."""
+    rng = np.random.default_rng(seed)
+    h = {0, 1, T - 1} | {c + o for c in range(2048, T, 2048) for o in (-1, 0)}
+    h |= set(rng.choice(T, 48 - len(h), replace=False).tolist())
+    vc = 4 * (((V + 7) // 8 + 3) // 4)
+    w = {0, V - 1} | {c * vc + o for c in range(1, 8) for o in (-1, 0)}
+    w |= set(int(t) for t in targets[:6])
+    w |= set(rng.choice(V, 48 - len(w), replace=False).tolist())
+    return np.array(sorted(h)[:48], np.int64), np.array(sorted(w)[:48], np.int64)
+
+
+def make_backward(cfg: int) -> dict:
+    """dH and dW rows of the fused backward on workload cfg with seeded upstream gradients
+    (synthetic.upstream_grads), and the magnitudes that bound their rounding."""
+    wl = S.WORKLOADS[cfg]
+    t0 = time.time()
+    case = S.fused_workload(cfg)
+    gold = np.load(golden_path(cfg), allow_pickle=False)
+    targets = gold["targets"]
+    T = case.h_bits.shape[0]
+    gl, ge = S.upstream_grads(cfg, T)
+    h_rows, w_rows = sampled_rows(T, wl.vocab, targets)
+    dh, dw, dh_mag, dw_mag = oracle.linear_grads_sampled(
+        S.bf16_bits_to_f32(case.h_bits), S.bf16_bits_to_f32(case.w_bits), targets,
+        wl.temperature, gl, ge, h_rows, w_rows)
+    path = os.path.join(HERE, f"fused_backward_{wl.name}.npz")
+    np.savez_compressed(path, h_rows=h_rows, w_rows=w_rows, dh=dh, dw=dw, dh_mag=dh_mag,
+                        dw_mag=dw_mag)
+    return {"file": os.path.basename(path), "n_tokens": int(T),
+            "upstream": "synthetic.upstream_grads(cfg, T)",
+            "sha256_g_logprob": sha256(gl), "sha256_g_entropy": sha256(ge),
+            "seconds": round(time.time() - t0, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--rows-per-block", type=int, default=512)
     ap.add_argument("--only", type=int, choices=CFGS, default=None)
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only the T=16384 backward rows (needs its forward golden)")
     args = ap.parse_args()
     manifest = {}
     if os.path.exists(MANIFEST):
@@ -111,10 +156,16 @@ def main():
                              "oracle.logprob_entropy, oracle.logits_grad on "
                              "synthetic.fused_workload(cfg)")
     manifest.setdefault("workloads", {})
+    manifest.setdefault("backward", {})
     for cfg in CFGS:
-        if args.only is not None and cfg != args.only:
+        if args.backward_only or (args.only is not None and cfg != args.only):
             continue
         manifest["workloads"][S.WORKLOADS[cfg].name] = make(cfg, args.rows_per_block)
+        with open(MANIFEST, "w") as f:
+            json.dump(manifest, f, indent=2)
+            f.write("\n")
+    if args.only in (None, 5):
+        manifest["backward"][S.WORKLOADS[5].name] = make_backward(5)
         with open(MANIFEST, "w") as f:
             json.dump(manifest, f, indent=2)
             f.write("\n")

@@ -127,8 +127,40 @@ def pin_fused_chain_rule_exact():
             assert abs(dw[v, k] - float(ex)) <= 1e-15
 
 
+def pin_sampled_fused_gradients_equal_the_full_ones():
+    """linear_grads_sampled (row blocks, selected dh and dW rows) equals the selected rows of
+    linear_grads (pinned above by exact rational sums) -- with several blocks, a masked row, an
+    out-of-range target and the last block short -- and its magnitudes are sum |grad| |W| and
+    sum |grad| |h| of exact brute-force sums."""
+    rng = np.random.default_rng(26)
+    T, d, V = 37, 8, 50
+    h = S.bf16_bits_to_f32(S.to_bf16_bits(rng.normal(size=(T, d)).astype(np.float32)))
+    w = S.bf16_bits_to_f32(S.to_bf16_bits(rng.normal(0, 0.5, size=(V, d)).astype(np.float32)))
+    h, w = h.astype(np.float64), w.astype(np.float64)
+    t = rng.integers(0, V, T)
+    t[4] = V + 3
+    gl, ge = rng.normal(size=T), rng.normal(size=T)
+    gl[4] = 0.0                     # out-of-range target without a logprob gradient
+    gl[9] = ge[9] = 0.0             # masked row
+    hr, wr = np.array([0, 4, 9, 16, 36]), np.array([0, 7, 49, int(t[3])])
+    dh_f, dw_f = OB.linear_grads(h, w, t, 0.7, gl, ge)
+    dh, dw, dh_mag, dw_mag = OB.linear_grads_sampled(h, w, t, 0.7, gl, ge, hr, wr, block=8)
+    assert np.abs(dh - dh_f[hr]).max() <= 1e-14 and np.abs(dw - dw_f[wr]).max() <= 1e-14
+    assert np.all(dh[2] == 0.0)
+    gx = OB.logits_grad(h @ w.T, t, 0.7, gl, ge)
+    for i, r in enumerate(hr):
+        for k in range(d):
+            ex = float(sum(abs(Fraction(gx[r, v])) * abs(Fraction(w[v, k])) for v in range(V)))
+            assert abs(dh_mag[i, k] - ex) <= 1e-14 * max(1.0, ex)
+    for i, v in enumerate(wr):
+        for k in range(d):
+            ex = float(sum(abs(Fraction(gx[r, v])) * abs(Fraction(h[r, k])) for r in range(T)))
+            assert abs(dw_mag[i, k] - ex) <= 1e-14 * max(1.0, ex)
+
+
 PINS = [pin_finite_differences, pin_torch_autograd, pin_closed_forms, pin_row_sums_zero,
-        pin_masking_and_nonfinite, pin_fused_chain_rule_exact]
+        pin_masking_and_nonfinite, pin_fused_chain_rule_exact,
+        pin_sampled_fused_gradients_equal_the_full_ones]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
