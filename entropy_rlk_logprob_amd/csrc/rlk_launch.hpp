@@ -28,6 +28,14 @@ __device__ __forceinline__ int64_t linear_block() {
   return (int64_t)blockIdx.z * gridDim.x + blockIdx.x;
 }
 
+// The wave's index within its workgroup (threadIdx.x / 64, the same on every lane of a
+// wave).  readfirstlane tells the compiler it is wave-uniform, so whatever derives from it
+// (tile offsets, chunk bounds, loop counts, branches) stays in scalar registers and scalar
+// branches instead of per-lane registers and exec masks.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // Canonical vocabulary partition shared by both paths: 8 chunks of Vc columns,
 // Vc = 4 * ceil(ceil(V / 8) / 4).
 inline int64_t chunk_cols(int64_t V) {
@@ -94,16 +102,22 @@ LinearWorkspace linear_workspace_layout(int64_t T, int64_t V, int S);
 
 hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream);
 
-// Fused-path backward (rlk_linear_bwd.hip).  Workspace: the forward layout, then the
-// regions below (byte offsets from the workspace base).
+// Fused-path backward (rlk_linear_bwd.hip).  It runs over the tokens in chunks of at most
+// kBackwardChunkTokens (each chunk: forward recompute if needed, logit gradient, its dH
+// rows, and its share of dW, accumulated onto the earlier chunks' in token order), so the
+// workspace is sized for one chunk: the forward layout, then the regions below (byte
+// offsets from the workspace base).
+constexpr int64_t kBackwardChunkTokens = 4096;
+
 struct LinearBackwardWorkspace {
-  int64_t Vp, Tp;  // V and T rounded up to multiples of 64 (K padding of the GEMMs)
-  size_t root;     // T root states
-  size_t rowc;     // T per-token gradient constants
-  size_t ht;       // H^T [d, Tp] bf16
-  size_t dx;       // dX [T, Vp] bf16, zero in columns [V, Vp)
-  size_t dxt;      // dX^T [V, Tp] bf16, zero in columns [T, Tp)
-  size_t part;     // 8 split-K partials of dH [T, d] fp32
+  int64_t chunk;   // tokens per chunk: min(T, kBackwardChunkTokens)
+  int64_t Vp, Tp;  // V and the chunk rounded up to multiples of 64 (K padding of the GEMMs)
+  size_t root;     // chunk root states
+  size_t rowc;     // chunk per-token gradient constants
+  size_t ht;       // H^T [d, Tp] bf16 of the chunk
+  size_t dx;       // dX [chunk, Vp] bf16, zero in columns [V, Vp)
+  size_t dxt;      // dX^T [V, Tp] bf16, zero in columns [chunk, Tp)
+  size_t part;     // 8 split-K partials of dH [chunk, d] fp32
   size_t total;
 };
 

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
   const int n_valid = (int)(v_hi - v_lo);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int wv = wave >> 2;  // vocab half (0, 1)
   const int wt = wave & 3;   // token quarter (0..3)
 
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_pair_kernel(
   }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int wv = wave >> 1;  // 128-row slice of the pair (0..3)
   const int wt = wave & 1;   // token half (0, 1)
   const int pt = wv >> 1;    // tile of the pair

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_tile_kernel(
                 smem, acc);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int wv = wave >> 2, wt = wave & 3;
   const int frow = lane & 31, fhalf = lane >> 5;
 #pragma unroll
@@ -239,8 +239,9 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, in
     p[(i / cols) * ld + i % cols] = 0.0f;
 }
 
-// Steps 4 and 5: C(m, n) = sum_k A[m, k] B[n, k] over the split's K range, in 256 x 256
-// tiles on the shared MFMA loop.  An operand is K-contiguous ([rows, K], row r at
+// Steps 4 and 5: C(m, n) = sum_k A[m, k] B[n, k] over the split's K range (ACCUM: C(m, n)
+// plus that sum, the accumulators starting from the stored C), in 256 x 256 tiles on the
+// shared MFMA loop.  An operand is K-contiguous ([rows, K], row r at
 // X + r ld) or K-major ([K, rows], k row at X + k ld; its k rows beyond k_last are
 // clamped, the other operand holding zeros there).  Stored row-major at C[m * ldc + n]
 // (32 lanes write 128 contiguous bytes of a row).  Split s (blockIdx.y) covers K steps
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, in
 // Tile order (tile_of): SHARE_B groups row tiles and runs column-tile-major within a group
 // (consecutive logical tiles share a B slice), else the reverse (they share an A slice):
 // the larger operand is fetched from HBM once and shared in an XCD's L2.
-template <bool A_KMAJOR, bool B_KMAJOR, bool SHARE_B>
+template <bool A_KMAJOR, bool B_KMAJOR, bool SHARE_B, bool ACCUM = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const uint16_t* __restrict__ A, int64_t lda, int64_t M, int64_t a_klast,
     const uint16_t* __restrict__ B, int64_t ldb, int64_t N, int64_t b_klast, int64_t K,
@@ -261,6 +262,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   const int64_t k_begin = (int64_t)blockIdx.y * steps * kBK;
   const int64_t k_end = min(k_begin + steps * kBK, K);
   const int nk = k_end > k_begin ? (int)((k_end - k_begin) / kBK) : 0;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int wv = wave >> 2, wt = wave & 3;
+  const int frow = lane & 31, fhalf = lane >> 5;
+  float* __restrict__ Cs = C + (int64_t)blockIdx.y * split_stride;
   floatx16 acc[4][2];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -268,6 +274,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+  if constexpr (ACCUM) {
+    // Continue the accumulation of the stored C: the same places the epilogue stores.
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t n = n_lo + wt * 64 + b * 32 + frow;
+      if (n >= N) continue;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int64_t m0 = m_lo + wv * 128 + a * 32 + 8 * g4 + 4 * fhalf;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (m0 + j < M) acc[a][b][4 * g4 + j] = Cs[(m0 + j) * ldc + n];
+        }
+    }
+  }
   if (nk > 0) {
     const int a_last = (int)min((int64_t)kTile, M - m_lo) - 1;
     const int b_last = (int)min((int64_t)kTile, N - n_lo) - 1;
@@ -275,11 +298,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const mma::Operand Bop{B_KMAJOR ? B + n_lo : B + n_lo * ldb, ldb, b_last, b_klast};
     mma::mma_tile_op<A_KMAJOR, B_KMAJOR>(Aop, Bop, k_begin, nk, smem, acc);
   }
-  float* __restrict__ Cs = C + (int64_t)blockIdx.y * split_stride;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wv = wave >> 2, wt = wave & 3;
-  const int frow = lane & 31, fhalf = lane >> 5;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int64_t n = n_lo + wt * 64 + b * 32 + frow;
@@ -326,21 +344,22 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 LinearBackwardWorkspace linear_backward_layout(int64_t T, int64_t V, int64_t d, int S) {
   LinearBackwardWorkspace L;
+  L.chunk = std::min<int64_t>(T, kBackwardChunkTokens);
   L.Vp = (V + kBK - 1) / kBK * kBK;
-  L.Tp = (T + kBK - 1) / kBK * kBK;
-  size_t off = align256(linear_workspace_layout(T, V, S).total);
+  L.Tp = (L.chunk + kBK - 1) / kBK * kBK;
+  size_t off = align256(linear_workspace_layout(L.chunk, V, S).total);
   L.root = off;
-  off += align256((size_t)T * sizeof(WireState));
+  off += align256((size_t)L.chunk * sizeof(WireState));
   L.rowc = off;
-  off += align256((size_t)T * sizeof(GradRowC));
+  off += align256((size_t)L.chunk * sizeof(GradRowC));
   L.ht = off;
   off += align256((size_t)d * (size_t)L.Tp * 2);
   L.dx = off;
-  off += align256((size_t)T * (size_t)L.Vp * 2);
+  off += align256((size_t)L.chunk * (size_t)L.Vp * 2);
   L.dxt = off;
   off += align256((size_t)V * (size_t)L.Tp * 2);
   L.part = off;
-  off += align256((size_t)kDhSplits * (size_t)T * (size_t)d * sizeof(float));
+  off += align256((size_t)kDhSplits * (size_t)L.chunk * (size_t)d * sizeof(float));
   L.total = off;
   return L;
 }
@@ -355,11 +374,16 @@ hipError_t launch_zero_f32(float* p, int64_t ld, int64_t rows, int64_t cols,
   return hipGetLastError();
 }
 
-hipError_t launch_linear_backward(const LinearArgs& fwd, const float* g_lp, const float* g_ent,
-                                  float* dH, int64_t ld_dh, float* dW, int64_t ld_dw,
-                                  const WireState* states, hipStream_t stream) {
+namespace {
+
+// One chunk of at most L.chunk tokens (the caller offsets every per-token pointer); accum:
+// dW continues the sum of the chunks before (their tokens precede this chunk's).
+hipError_t backward_chunk(const LinearArgs& fwd, const LinearBackwardWorkspace& L,
+                          const float* g_lp, const float* g_ent, float* dH, int64_t ld_dh,
+                          float* dW, int64_t ld_dw, const WireState* states, bool accum,
+                          hipStream_t stream) {
   const int64_t T = fwd.T, V = fwd.V, d = fwd.d;
-  const LinearBackwardWorkspace L = linear_backward_layout(T, V, d, fwd.S);
+  const int64_t Tp = (T + kBK - 1) / kBK * kBK;
   char* base = static_cast<char*>(fwd.ws);
   LinearArgs a = fwd;
   a.root = reinterpret_cast<WireState*>(base + L.root);
@@ -383,14 +407,14 @@ hipError_t launch_linear_backward(const LinearArgs& fwd, const float* g_lp, cons
   if (dx && L.Vp > V)
     hipLaunchKernelGGL(zero_cols_kernel, dim3(fill_blocks), dim3(256), 0, stream, dx, L.Vp, T, V,
                        L.Vp);
-  if (dxt && L.Tp > T)
-    hipLaunchKernelGGL(zero_cols_kernel, dim3(fill_blocks), dim3(256), 0, stream, dxt, L.Tp, V,
-                       T, L.Tp);
+  if (dxt && Tp > T)
+    hipLaunchKernelGGL(zero_cols_kernel, dim3(fill_blocks), dim3(256), 0, stream, dxt, Tp, V, T,
+                       Tp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   const int64_t tiles_x = ((V + kTile - 1) / kTile) * ((T + kTile - 1) / kTile);
   hipLaunchKernelGGL(dx_tile_kernel, split_grid((tiles_x + 7) / 8 * 8), dim3(kThreads), 0,
-                     stream, a.H, a.ldh, a.W, a.ldw, d, T, V, a.c, rc, dx, L.Vp, dxt, L.Tp);
+                     stream, a.H, a.ldh, a.W, a.ldw, d, T, V, a.c, rc, dx, L.Vp, dxt, Tp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   if (dH) {
@@ -412,21 +436,47 @@ hipError_t launch_linear_backward(const LinearArgs& fwd, const float* g_lp, cons
   }
   if (dW) {
     // dW[v, k] = sum_t dX^T[v, t] H^T[k, t]: A = dX^T (M = V), B = H^T (N = d; a transposed
-    // copy of H, small), both K-contiguous, K = Tp; row-tile-major within groups of 8
-    // column tiles, so that the tiles sharing a dX^T slice run together; stored row-major
-    // (32 lanes write 128 contiguous bytes of a dW row).  (Reading dX in place as a K-major
-    // A operand measured 0.6 ms slower at T = 2048, d = 4096, V = 151936 than writing dX^T
+    // copy of the chunk's H, small), both K-contiguous, K = Tp; row-tile-major within groups
+    // of 8 column tiles, so that the tiles sharing a dX^T slice run together; stored
+    // row-major (32 lanes write 128 contiguous bytes of a dW row).  After the first chunk
+    // the accumulators start from the stored dW, so the sum over all tokens runs in the
+    // one increasing K order whatever the chunking.  (Reading dX in place as a K-major A
+    // operand measured 0.6 ms slower at T = 2048, d = 4096, V = 151936 than writing dX^T
     // in step 3.)
     uint16_t* ht = reinterpret_cast<uint16_t*>(base + L.ht);
-    hipLaunchKernelGGL(transpose_pad_kernel, split_grid(L.Tp / 64, (unsigned)(d / 64)),
-                       dim3(256), 0, stream, a.H, a.ldh, T, d, ht, L.Tp, L.Tp);
+    hipLaunchKernelGGL(transpose_pad_kernel, split_grid(Tp / 64, (unsigned)(d / 64)), dim3(256),
+                       0, stream, a.H, a.ldh, T, d, ht, Tp, Tp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t tiles = ((V + kTile - 1) / kTile) * ((d + kTile - 1) / kTile);
-    hipLaunchKernelGGL((gemm_kernel<false, false, false>),
-                       split_grid((tiles + 7) / 8 * 8), dim3(kThreads), 0, stream, dxt,
-                       L.Tp, V, (int64_t)0, ht, L.Tp, d, (int64_t)0, L.Tp, L.Tp / kBK, dW, ld_dw,
-                       (int64_t)0);
+    if (accum)
+      hipLaunchKernelGGL((gemm_kernel<false, false, false, true>),
+                         split_grid((tiles + 7) / 8 * 8), dim3(kThreads), 0, stream, dxt, Tp, V,
+                         (int64_t)0, ht, Tp, d, (int64_t)0, Tp, Tp / kBK, dW, ld_dw, (int64_t)0);
+    else
+      hipLaunchKernelGGL((gemm_kernel<false, false, false>),
+                         split_grid((tiles + 7) / 8 * 8), dim3(kThreads), 0, stream, dxt, Tp, V,
+                         (int64_t)0, ht, Tp, d, (int64_t)0, Tp, Tp / kBK, dW, ld_dw, (int64_t)0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_linear_backward(const LinearArgs& fwd, const float* g_lp, const float* g_ent,
+                                  float* dH, int64_t ld_dh, float* dW, int64_t ld_dw,
+                                  const WireState* states, hipStream_t stream) {
+  const LinearBackwardWorkspace L = linear_backward_layout(fwd.T, fwd.V, fwd.d, fwd.S);
+  for (int64_t t0 = 0; t0 < fwd.T; t0 += L.chunk) {
+    LinearArgs a = fwd;
+    a.T = std::min<int64_t>(L.chunk, fwd.T - t0);
+    a.H = fwd.H + t0 * fwd.ldh;
+    a.targets = fwd.targets ? fwd.targets + t0 : nullptr;
+    const hipError_t e = backward_chunk(
+        a, L, g_lp ? g_lp + t0 : nullptr, g_ent ? g_ent + t0 : nullptr,
+        dH ? dH + t0 * ld_dh : nullptr, ld_dh, dW, ld_dw, states ? states + t0 : nullptr,
+        t0 > 0, stream);
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }

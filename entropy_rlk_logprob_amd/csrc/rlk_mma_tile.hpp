@@ -151,7 +151,7 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
   constexpr int kStage = (kARows + kBRows) * kBK * 2;  // 64 or 80 KiB
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int wv = wave / (8 / WA);  // A-side 128-row slice (0, 1; or 0..3)
   const int wt = wave % (8 / WA);  // B-side 64-row slice (0..3; or 0, 1)
   // Global -> LDS: direct 16-byte-per-lane loads into LDS (global_load_lds_dwordx4); one

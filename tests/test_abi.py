@@ -240,6 +240,11 @@ def test_linear_backward_workspace_and_validation(L):
     need = fwd + d * Tp * 2 + T * Vp * 2 + V * Tp * 2 + 8 * T * d * 4
     assert need <= ws <= need + (1 << 20)
     assert L.workspace_bytes(B.OP_LINEAR_BACKWARD, 0, V, d, 1) == 0
+    # the backward runs in token chunks of 4096: its workspace stops growing there
+    ws4k = L.workspace_bytes(B.OP_LINEAR_BACKWARD, 4096, V, d, 1)
+    assert ws4k > ws
+    for big in (4097, 8192, 16384, 1 << 20):
+        assert L.workspace_bytes(B.OP_LINEAR_BACKWARD, big, V, d, 1) == ws4k, big
     with pytest.raises(B.RlkError):
         L.workspace_bytes(B.OP_LINEAR_BACKWARD, T, V, 100, 1)         # d not a multiple of 64
     call = lambda **kw: call_linear_backward(L, **kw)  # noqa: E731

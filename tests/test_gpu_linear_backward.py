@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
+from entropy_rlk_logprob_amd import binding as B
 from entropy_rlk_logprob_amd import synthetic as S
 from tests.helpers import announce, bits_dev, bitwise_equal, dev
 
@@ -207,3 +208,79 @@ def test_strided_operands_give_the_same_bits(lib):
                                          ged)
     assert torch.equal(dh.view(torch.int32), dh0.view(torch.int32))
     assert torch.equal(dw.view(torch.int32), dw0.view(torch.int32))
+
+
+def test_chunked_weight_gradient_continues_the_earlier_chunks(lib):
+    """The backward runs over the tokens in chunks of 4096; each chunk's share of dW is
+    accumulated onto the stored sum of the chunks before it (the MFMA accumulators start from
+    it), so dW is one fp32 sum in increasing token order whatever the chunking.  A row whose
+    two upstream gradients are 0 has an all-zero logit gradient and adds exact zeros, so
+    masking the rows of some chunks must give the dW of the other rows run alone (equal
+    values; only the sign of a zero may differ), and the unmasked rows' dH bits."""
+    T, d, V = 8300, 128, 1500       # chunks of 4096, 4096 and 108 tokens
+    announce(f"linear backward T={T} d={d} V={V} (token chunks)")
+    case = S.random_fused_case(T, d, V, seed=9700, h_sigma=1.0, w_sigma=3.0 / math.sqrt(d))
+    gl, ge = weights(T, 9701)
+    hd, wd, td = bits_dev(case.h_bits), bits_dev(case.w_bits), dev(case.targets)
+    h, w = f32(case.h_bits), f32(case.w_bits)
+    gx = oracle.logits_grad(h @ w.T, case.targets, 1.0, gl, ge)
+    dh, dw = run_bwd(lib, hd, wd, td, 1.0, 1, dev(gl), dev(ge))
+    check(dh, gx @ w, bound(gx, w, -(-V // 64) * 64))
+    check(dw, gx.T @ h, bound(gx.T, h, -(-T // 64) * 64))
+    for lo, hi in ((0, 4096), (4096, T), (3000, 5000), (8192, T)):
+        announce(f"linear backward: rows [{lo},{hi}) unmasked, alone vs in the batch")
+        glm, gem = np.zeros_like(gl), np.zeros_like(ge)
+        glm[lo:hi], gem[lo:hi] = gl[lo:hi], ge[lo:hi]
+        dh_m, dw_m = run_bwd(lib, hd, wd, td, 1.0, 1, dev(glm), dev(gem))
+        dh_a, dw_a = run_bwd(lib, hd[lo:hi], wd, td[lo:hi], 1.0, 1, dev(gl[lo:hi]),
+                             dev(ge[lo:hi]))
+        assert np.array_equal(dw_m, dw_a), (lo, hi)
+        assert bitwise_equal(dh_m[lo:hi], dh_a) and np.all(dh_m[:lo] == 0) and \
+            np.all(dh_m[hi:] == 0)
+
+
+def test_large_ragged_batch_sampled_rows_vs_oracle(lib):
+    """T = 16384, d = 4096, V = 151936, tau = 0.7 with the golden targets and seeded upstream
+    gradients (every 7th row masked): 48 rows of dH and 48 rows of dW against the fp64 oracle
+    (tests/golden, oracle.linear_grads_sampled) within the bf16-rounding + fp32-accumulation
+    bound; vocab split 4 bitwise equal to split 1.  The workspace is that of one 4096-token
+    chunk (the call runs four)."""
+    import torch
+    from tests.helpers import load_fused_golden
+    wl = S.WORKLOADS[5]
+    fwd = load_fused_golden(wl.name)
+    import json
+    import os
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    with open(os.path.join(here, "fused_goldens.json")) as f:
+        meta = json.load(f)["backward"][wl.name]
+    with np.load(os.path.join(here, meta["file"]), allow_pickle=False) as z:
+        g = {k: z[k] for k in z.files}
+    announce(f"generating fused workload {wl.name} (backward)")
+    case = S.fused_workload(5)
+    T, d = case.h_bits.shape
+    V = case.w_bits.shape[0]
+    gl, ge = S.upstream_grads(5, T)
+    assert lib.workspace_bytes(B.OP_LINEAR_BACKWARD, T, V, d, 1) == \
+        lib.workspace_bytes(B.OP_LINEAR_BACKWARD, 4096, V, d, 1)
+    hd, wd, td = bits_dev(case.h_bits), bits_dev(case.w_bits), dev(fwd["targets"])
+    gld, ged = dev(gl), dev(ge)
+    announce("linear backward T=16384 split=1")
+    dh, dw = lib.linear_logprob_backward(hd, wd, td, 0.7, 1, gld, ged)
+    torch.cuda.synchronize()
+    hr, wr = torch.from_numpy(g["h_rows"]).cuda(), torch.from_numpy(g["w_rows"]).cuda()
+    dh_s, dw_s = dh[hr].cpu().numpy(), dw[wr].cpu().numpy()
+    Vp, Tp = -(-V // 64) * 64, -(-T // 64) * 64
+    check(dh_s, g["dh"], (2.0 ** -8 + Vp * 2.0 ** -24) * g["dh_mag"] + 1e-30)
+    check(dw_s, g["dw"], (2.0 ** -8 + Tp * 2.0 ** -24) * g["dw_mag"] + 1e-30)
+    rel_dh = np.abs(dh_s - g["dh"]).max() / np.abs(g["dh"]).max()
+    rel_dw = np.abs(dw_s - g["dw"]).max() / np.abs(g["dw"]).max()
+    print(f"[T=16384 backward] max |err| / max |ref|: dH {rel_dh:.2e}, dW {rel_dw:.2e}",
+          flush=True)
+    masked = np.flatnonzero((gl[g["h_rows"]] == 0) & (ge[g["h_rows"]] == 0))
+    assert masked.size > 0 and np.all(dh_s[masked] == 0)
+    announce("linear backward T=16384 split=4")
+    dh4, dw4 = lib.linear_logprob_backward(hd, wd, td, 0.7, 4, gld, ged)
+    torch.cuda.synchronize()
+    assert torch.equal(dh4.view(torch.int32), dh.view(torch.int32))
+    assert torch.equal(dw4.view(torch.int32), dw.view(torch.int32))
