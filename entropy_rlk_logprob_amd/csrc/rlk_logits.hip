@@ -7,7 +7,7 @@
 //     a lane's quads k = 0, 1, 2, ... (q = lane + 64 k) are grouped four at a time into
 //     16-element leaves;
 //   * groups are folded into the lane's state in increasing k (fold_group): the state
-//     keeps a reference m (the lane's running max, up to one unit of c (x - m)) and fp64
+//     keeps a reference m (the lane's running max, up to 8 units of c (x - m)) and fp64
 //     sums relative to it; a group whose max exceeds m by more than that first rebases
 //     the sums to its max, then its fp32 terms 2^{c (x - m)} and 2^{c (x - m)} c (x - m)
 //     are summed pairwise (within each quad, then quad pairs) and added in;
@@ -20,6 +20,8 @@
 // chunks of the shard); each lane streams 16-byte loads (bf16: 8-byte) whose 64 lanes
 // cover 1 KiB (512 bytes) of contiguous HBM per instruction.
 // The loads carry the non-temporal hint: every logit is read exactly once.
+
+#include <type_traits>
 
 #include "rlk_launch.hpp"
 #include "rlk_state.hpp"
@@ -46,17 +48,20 @@ template <typename E> struct RawGroup;
 template <> struct RawGroup<float> { f32x4 q[4]; };
 template <> struct RawGroup<uint16_t> { u32x2 q[4]; };
 
+// Full group: four quad loads at 32-bit byte offsets from the chunk's first column, which
+// is the same for the whole wave, so they take the scalar-base form (one address add per
+// group, the four loads 64 quads apart by immediate offsets).  A chunk spans less than 2^30
+// bytes (V < 2^31 columns, 8 chunks), so the offsets fit.
 template <typename E>
 __device__ __forceinline__ void load_raw(const E* __restrict__ p, int lane, int g,
                                          RawGroup<E>& r) {
+  using Q = std::remove_reference_t<decltype(r.q[0])>;
+  const char* b = reinterpret_cast<const char*>(p);
+  const uint32_t off = (uint32_t)(lane + 256 * g) * (uint32_t)sizeof(Q);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = lane + 64 * (4 * g + i);
-    if constexpr (sizeof(E) == 4)
-      r.q[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + q);
-    else
-      r.q[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p) + q);
-  }
+  for (int i = 0; i < 4; ++i)
+    r.q[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const Q*>(b + off + (uint32_t)(i * 64 * (int)sizeof(Q))));
 }
 
 template <typename E>
@@ -105,20 +110,38 @@ __device__ __forceinline__ void load_group_masked(const E* __restrict__ p, int l
 }
 
 // Wide-load form of a chunk's last (partial) group: a quad wholly inside the chunk takes
-// the wide load, the others element loads with -inf beyond column n (the identity's
-// contribution; bf16 -inf is 0xff80).  It yields the values load_group_masked yields, so
-// the leaf sees the same bits either way.
+// the wide load, a quad wholly beyond it is four -inf (the identity's contribution; bf16
+// -inf is 0xff80), and only a quad that straddles column n loads elements.  It yields the
+// values load_group_masked yields, so the leaf sees the same bits either way.
 template <typename E>
 __device__ __forceinline__ void load_raw_masked(const E* __restrict__ p, int lane, int g, int n,
                                                 RawGroup<E>& r) {
+  using Q = std::remove_reference_t<decltype(r.q[0])>;
+  Q neg;  // four -inf elements
+  if constexpr (sizeof(E) == 4)
+    neg = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+  else
+    neg = u32x2{0xff80ff80u, 0xff80ff80u};
+  if ((n & 3) == 0) {
+    // Every quad lies wholly inside the chunk or wholly beyond it (the common case: the
+    // chunk width is a multiple of 4 unless it is a row's short last chunk).
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = lane + 64 * (4 * g + i);
+      if (4 * q < n)
+        r.q[i] = __builtin_nontemporal_load(reinterpret_cast<const Q*>(p) + q);
+      else
+        r.q[i] = neg;
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int q = lane + 64 * (4 * g + i);
     if (4 * q + 4 <= n) {
-      if constexpr (sizeof(E) == 4)
-        r.q[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + q);
-      else
-        r.q[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p) + q);
+      r.q[i] = __builtin_nontemporal_load(reinterpret_cast<const Q*>(p) + q);
+    } else if (4 * q >= n) {
+      r.q[i] = neg;
     } else if constexpr (sizeof(E) == 4) {
       f32x4 v;
       v.x = (4 * q + 0 < n) ? __builtin_nontemporal_load(p + 4 * q + 0) : kNegInf;
@@ -139,12 +162,17 @@ __device__ __forceinline__ void load_raw_masked(const E* __restrict__ p, int lan
 // A lane's running state over its groups: (m, s, u) of everything folded so far with
 // s and u relative to the reference m, and ref = m, or 0 while m = -inf (every value
 // seen so far is -inf and contributes 0).  A group whose max g exceeds the reference by
-// more than one unit of a, c (g - m) > 1, first rebases the sums to g in fp64:
-// s <- s 2^d, u <- (u + d s) 2^d with d = c (m - g); its 16 terms 2^a and 2^a a,
-// a = c (x - ref) <= 1, are then summed pairwise in fp32 (within each quad, then quad
-// pairs) and added to s and u.  So m stays within ln(2) tau of the lane's max, every
-// rebase at least halves the weight of what came before (a long run of tiny rebases would
-// otherwise compound the rounding of their factors), and the sums stay far from overflow.
+// more than kRebaseUnits units of a, c (g - m) > kRebaseUnits, first rebases the sums to g
+// in fp64: s <- s 2^d, u <- (u + d s) 2^d with d = c (m - g); its 16 terms 2^a and 2^a a,
+// a = c (x - ref) <= kRebaseUnits, are then summed pairwise in fp32 (within each quad, then
+// quad pairs) and added to s and u.  So m stays within kRebaseUnits ln(2) tau of the lane's
+// max, every rebase divides the weight of what came before by at least 2^kRebaseUnits (a
+// long run of tiny rebases would otherwise compound the rounding of their factors), and
+// the terms stay at most 2^kRebaseUnits.  The rebase is a per-lane branch, so a wave runs
+// it whenever any of its lanes needs it: with a margin of 1 unit that was nearly every
+// group on N(0, 3^2) logits, with 8 about a third of them.
+constexpr float kRebaseUnits = 8.0f;
+
 struct LaneFold {
   State st;
   float ref;
@@ -156,8 +184,8 @@ __device__ __forceinline__ void fold_group(LaneFold& f, const float* v, float c)
   float gm = v[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) gm = fmaxf(gm, v[i]);
-  if ((gm - f.st.m) * c > 1.0f) {      // false for NaN: a NaN group poisons s below
-    const float d = (f.st.m - gm) * c;  // < -1; -inf when m = -inf or gm = +inf
+  if ((gm - f.st.m) * c > kRebaseUnits) {  // false for NaN: a NaN group poisons s below
+    const float d = (f.st.m - gm) * c;  // < -kRebaseUnits; -inf when m = -inf or gm = +inf
     const double scale = (double)exp2_hw(d);
     const double dc = (double)fmaxf(d, -kMaxFloat);  // keeps 0 * (-inf) out of u
     f.st.u = (f.st.u + dc * f.st.s) * scale;
@@ -244,7 +272,7 @@ void row_reduce_kernel(
   const int64_t row = linear_block();
   if (row >= T) return;
   const int shard = blockIdx.y;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int lane = threadIdx.x & 63;
   const E* __restrict__ base = X + row * ld;
   const ChunkRef<E> A = chunk_ref(base, (int64_t)shard * CPS + wave, Vc, V);
@@ -260,46 +288,63 @@ void row_reduce_kernel(
     // loads of the next group are in flight while a group is folded, across the chunk
     // boundary and into each chunk's partial last group, so no load latency is exposed
     // before the end of the stream.  (Deeper prefetch measured no faster.)
-    const int n = A.n_groups + B.n_groups;
-    auto issue = [&](int j, RawGroup<E>& r) {
-      if (j < A.n_groups)
-        issue_group(A.p, lane, j, A.n, A.n_full, r);
-      else
-        issue_group(B.p, lane, j - A.n_groups, B.n, B.n_full, r);
-    };
-    LaneFold f = lane_fold_init();
-    auto fold = [&](int j, const RawGroup<E>& r) {
-      if (j == A.n_groups) {
-        sa = f.st;
-        f = lane_fold_init();
-      }
-      fold_raw(f, r, c);
-    };
     if constexpr (CPW == 2) {
-      // Unrolled by two: the buffers swap roles without copies.
-      RawGroup<E> b0, b1;
-      if (n > 0) issue(0, b0);
-      if (n > 1) issue(1, b1);
-      for (int j = 0; j < n; j += 2) {
-        fold(j, b0);
-        if (j + 2 < n) issue(j + 2, b0);
-        if (j + 1 >= n) break;
-        fold(j + 1, b1);
-        if (j + 3 < n) issue(j + 3, b1);
+      // The wave's two chunks side by side: group g of A, then group g of B, each folded
+      // into its own lane state in its own increasing order (so a chunk's bits are those of
+      // a wave that folds it alone).  Each chunk streams through two buffers, so the next
+      // two groups of each chunk are in flight while a group is folded; a buffer is
+      // reloaded right after it is folded (unrolled by two: no register copies).
+      LaneFold fa = lane_fold_init(), fb = lane_fold_init();
+      RawGroup<E> ra0, ra1, rb0, rb1;
+      if (A.n_groups > 0) issue_group(A.p, lane, 0, A.n, A.n_full, ra0);
+      if (B.n_groups > 0) issue_group(B.p, lane, 0, B.n, B.n_full, rb0);
+      if (A.n_groups > 1) issue_group(A.p, lane, 1, A.n, A.n_full, ra1);
+      if (B.n_groups > 1) issue_group(B.p, lane, 1, B.n, B.n_full, rb1);
+      const int n = max(A.n_groups, B.n_groups);
+      auto step = [&](int g, LaneFold& f, RawGroup<E>& r, const ChunkRef<E>& C) {
+        if (g < C.n_groups) {
+          fold_raw(f, r, c);
+          if (g + 2 < C.n_groups) issue_group(C.p, lane, g + 2, C.n, C.n_full, r);
+        }
+      };
+      for (int g = 0; g < n; g += 2) {
+        step(g, fa, ra0, A);
+        step(g, fb, rb0, B);
+        step(g + 1, fa, ra1, A);
+        step(g + 1, fb, rb1, B);
       }
-    } else {
+      sa = fa.st;
+      sb = fb.st;
+    } else if constexpr (sizeof(E) == 4) {
+      // fp32, eight waves per SIMD within 64 VGPRs: the next group in flight while a group
+      // is folded (a second buffer pair would spill).
+      const int n = A.n_groups;
+      LaneFold f = lane_fold_init();
       RawGroup<E> cur, nxt;
-      if (n > 0) issue(0, cur);
+      if (n > 0) issue_group(A.p, lane, 0, A.n, A.n_full, cur);
       for (int j = 0; j < n; ++j) {
-        if (j + 1 < n) issue(j + 1, nxt);
-        fold(j, cur);
+        if (j + 1 < n) issue_group(A.p, lane, j + 1, A.n, A.n_full, nxt);
+        fold_raw(f, cur, c);
         cur = nxt;
       }
-    }
-    if (n > A.n_groups)
-      sb = f.st;
-    else
       sa = f.st;
+    } else {
+      // One chunk through two buffers (unrolled by two: no register copies), the next two
+      // groups in flight while a group is folded.
+      const int n = A.n_groups;
+      LaneFold f = lane_fold_init();
+      RawGroup<E> r0, r1;
+      if (n > 0) issue_group(A.p, lane, 0, A.n, A.n_full, r0);
+      if (n > 1) issue_group(A.p, lane, 1, A.n, A.n_full, r1);
+      for (int g = 0; g < n; g += 2) {
+        fold_raw(f, r0, c);
+        if (g + 2 < n) issue_group(A.p, lane, g + 2, A.n, A.n_full, r0);
+        if (g + 1 >= n) break;
+        fold_raw(f, r1, c);
+        if (g + 3 < n) issue_group(A.p, lane, g + 3, A.n, A.n_full, r1);
+      }
+      sa = f.st;
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {

@@ -74,7 +74,7 @@ typedef enum {
 /*
  * A row's reduction state, as the forward calls can save it for the backward calls (the
  * analogue of saving the log-sum-exp): 24 bytes, 8-byte aligned.  Its contents are the
- * canonical state the forward reduced to (a reference logit m within ln(2) temperature of
+ * canonical state the forward reduced to (a reference logit m within 8 ln(2) temperature of
  * the row's max, and in fp64 s = sum 2^a, u = sum 2^a a with
  * a = log2(e) (x - m) / temperature) plus the target's logit; callers treat it as opaque.
  * It depends on the logits and the temperature, not on vocab_splits.

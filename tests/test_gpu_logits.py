@@ -217,14 +217,17 @@ def test_nonfinite_rows_and_targets(lib):
 @pytest.mark.parametrize("tau", [1.0, 0.7])
 def test_monotone_and_sawtooth_rows_vs_oracle(lib, tau):
     """Rows whose running max rises at (almost) every group of every lane, which makes each
-    lane rebase its sums again and again, next to falling, sawtooth and offset rows."""
+    lane rebase its sums again and again, next to falling, sawtooth and offset rows.  A
+    lane's consecutive groups are 1024 columns apart, so 5.3e-3 tau and 5.5e-3 tau per column
+    rise by just under and just over the 8 units of c (x - m) after which a lane rebases:
+    terms up to 2^8 in every group, and a rebase at every group."""
     V = 151936
     i = np.arange(V, dtype=np.float64)
     rows = [1e-6 * i, 1e-5 * i, 3e-6 * i - 0.2, 1e-3 * i, -1e-5 * i, (i % 1024) * 1e-3,
-            1000.0 + 1e-5 * i, -50.0 + 2e-4 * i]
+            1000.0 + 1e-5 * i, -50.0 + 2e-4 * i, 5.3e-3 * tau * i, 5.5e-3 * tau * i]
     x = np.stack(rows).astype(np.float32)
     T = x.shape[0]
-    t = np.array([V - 1, 0, V // 2, V - 2, 0, 1023, 77, V - 1])
+    t = np.array([V - 1, 0, V // 2, V - 2, 0, 1023, 77, V - 1, V - 3, V - 700])
     announce(f"logits monotone and sawtooth rows V={V} tau={tau}")
     olp, oent = oracle.logprob_entropy(x, t, tau)
     ref = None
