@@ -301,13 +301,29 @@ void row_reduce_kernel(
       if (A.n_groups > 1) issue_group(A.p, lane, 1, A.n, A.n_full, ra1);
       if (B.n_groups > 1) issue_group(B.p, lane, 1, B.n, B.n_full, rb1);
       const int n = max(A.n_groups, B.n_groups);
-      auto step = [&](int g, LaneFold& f, RawGroup<E>& r, const ChunkRef<E>& C) {
-        if (g < C.n_groups) {
+      // Main loop: while both chunks' next groups are full, only wide loads are issued,
+      // so every iteration issues the same loads in the same order and the compiler can
+      // wait for exactly the group being folded (with the masked loads of a chunk's last
+      // group in the same loop it waited for every load in flight at each group).
+      const int n_full = min(A.n_full, B.n_full);
+      int g = 0;
+      for (; g + 3 < n_full; g += 2) {
+        fold_raw(fa, ra0, c);
+        load_raw(A.p, lane, g + 2, ra0);
+        fold_raw(fb, rb0, c);
+        load_raw(B.p, lane, g + 2, rb0);
+        fold_raw(fa, ra1, c);
+        load_raw(A.p, lane, g + 3, ra1);
+        fold_raw(fb, rb1, c);
+        load_raw(B.p, lane, g + 3, rb1);
+      }
+      auto step = [&](int j, LaneFold& f, RawGroup<E>& r, const ChunkRef<E>& C) {
+        if (j < C.n_groups) {
           fold_raw(f, r, c);
-          if (g + 2 < C.n_groups) issue_group(C.p, lane, g + 2, C.n, C.n_full, r);
+          if (j + 2 < C.n_groups) issue_group(C.p, lane, j + 2, C.n, C.n_full, r);
         }
       };
-      for (int g = 0; g < n; g += 2) {
+      for (; g < n; g += 2) {
         step(g, fa, ra0, A);
         step(g, fb, rb0, B);
         step(g + 1, fa, ra1, A);
@@ -322,7 +338,13 @@ void row_reduce_kernel(
       LaneFold f = lane_fold_init();
       RawGroup<E> cur, nxt;
       if (n > 0) issue_group(A.p, lane, 0, A.n, A.n_full, cur);
-      for (int j = 0; j < n; ++j) {
+      int j = 0;
+      for (; j + 1 < A.n_full; ++j) {  // next group full: wide loads only (see above)
+        load_raw(A.p, lane, j + 1, nxt);
+        fold_raw(f, cur, c);
+        cur = nxt;
+      }
+      for (; j < n; ++j) {
         if (j + 1 < n) issue_group(A.p, lane, j + 1, A.n, A.n_full, nxt);
         fold_raw(f, cur, c);
         cur = nxt;
@@ -336,7 +358,14 @@ void row_reduce_kernel(
       RawGroup<E> r0, r1;
       if (n > 0) issue_group(A.p, lane, 0, A.n, A.n_full, r0);
       if (n > 1) issue_group(A.p, lane, 1, A.n, A.n_full, r1);
-      for (int g = 0; g < n; g += 2) {
+      int g = 0;
+      for (; g + 3 < A.n_full; g += 2) {  // wide loads only (see above)
+        fold_raw(f, r0, c);
+        load_raw(A.p, lane, g + 2, r0);
+        fold_raw(f, r1, c);
+        load_raw(A.p, lane, g + 3, r1);
+      }
+      for (; g < n; g += 2) {
         fold_raw(f, r0, c);
         if (g + 2 < n) issue_group(A.p, lane, g + 2, A.n, A.n_full, r0);
         if (g + 1 >= n) break;
