@@ -71,7 +71,8 @@ FUSED_WARMUP_CALLS = 60
 MFMA_PROBE_BLOCKS = 256
 MFMA_PROBE_ITERS = 32768
 TRAFFIC_SOURCES = ["entropy_rlk_logprob_amd/csrc/rlk_logits.hip",
-                   "entropy_rlk_logprob_amd/csrc/rlk_state.hpp"]
+                   "entropy_rlk_logprob_amd/csrc/rlk_state.hpp",
+                   "entropy_rlk_logprob_amd/csrc/rlk_launch.hpp"]
 
 
 def log(msg: str):
