@@ -42,17 +42,26 @@ using mma::kThreads;
 constexpr int kTile = 256;
 constexpr int kDhSplits = 8;
 
+// Per-token constants of the logit gradient: the root state's m and log2 s, the entropy H,
+// the upstream gradients times 1/tau (bgl, bge), the row mode and the value a row that is
+// not computed takes (0 for a row whose upstream gradients are both 0, NaN for a row whose
+// forward outputs are NaN).
 struct GradRowC {
-  float m, lg2s, H, beta, gl, ge;
+  float m, lg2s, H, bgl, bge, fill;
   int32_t mode;  // 0 compute, 1 all-zero row, 2 NaN row
   int32_t pad;
   int64_t t;
 };
 
-__device__ __forceinline__ uint16_t to_bf16_rne(float f) {
-  const uint32_t b = __float_as_uint(f);
-  if ((b & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // quiet NaN
-  return (uint16_t)((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to bf16 (round to nearest even) and packed, the first in the low
+// half: v_cvt_pk_bf16_f32.  On every one of the 2^32 fp32 bit patterns it gives the bits of
+// the plain round-to-nearest-even formula (b + 0x7fff + ((b >> 16) & 1)) >> 16, and a NaN
+// for a NaN (checked exhaustively on the device).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
 }
 
 __global__ __launch_bounds__(256) void row_consts_kernel(
@@ -62,40 +71,47 @@ __global__ __launch_bounds__(256) void row_consts_kernel(
   const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (row >= T) return;
   GradRowC r;
-  r.gl = g_lp ? g_lp[row] : 0.0f;
-  r.ge = g_ent ? g_ent[row] : 0.0f;
+  const float gl = g_lp ? g_lp[row] : 0.0f;
+  const float ge = g_ent ? g_ent[row] : 0.0f;
   r.t = targets ? targets[row] : -1;
-  r.beta = (float)beta;
+  r.bgl = (float)beta * gl;
+  r.bge = (float)beta * ge;
   r.m = 0.0f;
   r.lg2s = 0.0f;
   r.H = 0.0f;
   r.pad = 0;
-  if (r.gl == 0.0f && r.ge == 0.0f) {
+  if (gl == 0.0f && ge == 0.0f) {
     r.mode = 1;
   } else {
     const State st = from_wire(root[row]);
     const bool ok =
         (st.m != kNegInf) && (st.s > 0.0) && (st.s < __builtin_inf()) && (st.u == st.u);
     const bool has = (r.t >= 0) && (r.t < V);
-    r.mode = (!ok || (!has && r.gl != 0.0f)) ? 2 : 0;
+    r.mode = (!ok || (!has && gl != 0.0f)) ? 2 : 0;
     if (r.mode == 0) {
       r.m = st.m;
       r.lg2s = (float)log2(st.s);
       r.H = (float)(log(st.s) - kLn2 * (st.u / st.s));
     }
   }
+  r.fill = r.mode == 1 ? 0.0f : __builtin_nanf("");
   out[row] = r;
 }
 
-// Gradient of one logit (same formula and fp32 steps as the logits-path backward).
+// Gradient of one logit: with a = c (x - m), q = a - log2 s (log2 p), p = 2^q,
+//   g = bgl (delta - p) - bge p (q ln 2 + H)      (bgl = g_lp / tau, bge = g_ent / tau),
+// p (ln p + H) taken as 0 where p = 0.  Every logit of a token is formed by these same fp32
+// steps whatever tile it falls in, so a row of dX, and so of dH, does not depend on the
+// batch.
 __device__ __forceinline__ float logit_grad(float x, bool is_target, const GradRowC& r, float c) {
-  if (r.mode != 0) return r.mode == 1 ? 0.0f : __builtin_nanf("");
-  const float a = (x - r.m) * c;
-  const float q = a - r.lg2s;
+  const float q = (x - r.m) * c - r.lg2s;
   const float p = exp2_hw(q);
-  const float lnp = q * 0.693147180559945309f;
-  const float ent = mul_zero_wins(p, lnp + r.H);
-  return r.beta * (r.gl * ((is_target ? 1.0f : 0.0f) - p) - r.ge * ent);
+  const float ent = mul_zero_wins(p, __builtin_fmaf(q, 0.693147180559945309f, r.H));
+  float g = __builtin_fmaf(r.bgl, (is_target ? 1.0f : 0.0f) - p, -(r.bge * ent));
+  // g is formed on every lane and then selected: left to itself the compiler branches around
+  // the formula per logit (an exec-mask branch each time) for the rows that take r.fill.
+  asm volatile("" : "+v"(g));
+  return r.mode == 0 ? g : r.fill;
 }
 
 // Output tile id -> (row tile, column tile): column tiles in groups of 8, row-tile-major
@@ -130,6 +146,46 @@ __global__ __launch_bounds__(kThreads, 1) void dx_tile_kernel(
   const int wave = wave_id();
   const int wv = wave >> 2, wt = wave & 3;
   const int frow = lane & 31, fhalf = lane >> 5;
+  // Lane (wv, wt, lane) holds, for tokens t_lo + wt 64 + b 32 + frow (b = 0, 1), the logits
+  // of rows v_lo + wv 128 + a 32 + 8 g4 + 4 fhalf + j (a, g4, j = 0..3) in acc[a][b][4 g4 + j].
+  const int64_t row0 = v_lo + wv * 128 + 4 * fhalf;  // this lane's first row
+  if (v_lo + kTile <= V && t_lo + kTile <= T) {
+    // Full tile: no bounds tests.  dX rows are stored 8 bytes (4 rows) at a time from a
+    // per-lane base with immediate offsets.  A dX^T element of row row0 + off + j sits at the
+    // wave-uniform base of row v_lo + wv 128 + off (scalar registers) plus a per-lane 32-bit
+    // byte offset, one per j, fixed for the token.
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t tok = t_lo + wt * 64 + b * 32 + frow;
+      const GradRowC r = rc[tok];
+      const int tgt = (r.t >= row0 && r.t < row0 + 128) ? (int)(r.t - row0) : -1;
+      uint16_t* const xrow = dX ? dX + tok * ldx + row0 : nullptr;
+      uint32_t xt_off[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xt_off[j] = (uint32_t)(((4 * fhalf + j) * ldxt + (tok - t_lo)) * 2);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int off = a * 32 + 8 * g4;  // row offset from row0 (compile-time)
+          float g[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) g[j] = logit_grad(acc[a][b][4 * g4 + j], tgt == off + j, r, c);
+          const uint32_t w0 = pack_bf16(g[0], g[1]), w1 = pack_bf16(g[2], g[3]);
+          if (dX) *reinterpret_cast<uint2*>(xrow + off) = make_uint2(w0, w1);
+          if (dXT) {
+            char* rb = reinterpret_cast<char*>(dXT + (v_lo + wv * 128 + off) * ldxt + t_lo);
+            const uint16_t h[4] = {(uint16_t)w0, (uint16_t)(w0 >> 16), (uint16_t)w1,
+                                   (uint16_t)(w1 >> 16)};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) *reinterpret_cast<uint16_t*>(rb + xt_off[j]) = h[j];
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int64_t tok = t_lo + wt * 64 + b * 32 + frow;
@@ -139,18 +195,18 @@ __global__ __launch_bounds__(kThreads, 1) void dx_tile_kernel(
     for (int a = 0; a < 4; ++a) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int64_t v0 = v_lo + wv * 128 + a * 32 + 8 * g4 + 4 * fhalf;
+        const int64_t v0 = row0 + a * 32 + 8 * g4;
         if (v0 >= V) continue;
-        uint16_t bits[4];
+        float g[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bits[j] = to_bf16_rne(logit_grad(acc[a][b][4 * g4 + j], v0 + j == r.t, r, c));
+        for (int j = 0; j < 4; ++j) g[j] = logit_grad(acc[a][b][4 * g4 + j], v0 + j == r.t, r, c);
+        const uint32_t w0 = pack_bf16(g[0], g[1]), w1 = pack_bf16(g[2], g[3]);
+        const uint16_t bits[4] = {(uint16_t)w0, (uint16_t)(w0 >> 16), (uint16_t)w1,
+                                  (uint16_t)(w1 >> 16)};
         if (dX) {
           uint16_t* dst = dX + tok * ldx + v0;
           if (v0 + 4 <= V) {
-            const uint2 w2 = make_uint2((uint32_t)bits[0] | ((uint32_t)bits[1] << 16),
-                                        (uint32_t)bits[2] | ((uint32_t)bits[3] << 16));
-            *reinterpret_cast<uint2*>(dst) = w2;
+            *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
           } else {
             for (int j = 0; j < 4 && v0 + j < V; ++j) dst[j] = bits[j];
           }
