@@ -11,7 +11,9 @@
 //     sums relative to it; a group whose max exceeds m by more than that first rebases
 //     the sums to its max, then its fp32 terms 2^{c (x - m)} and 2^{c (x - m)} c (x - m)
 //     are summed pairwise (within each quad, then quad pairs) and added in;
-//   * lanes: xor-butterfly (32, 16, 8, 4, 2, 1); chunks: ((0,1),(2,3)),((4,5),(6,7)).
+//   * lanes: wave_merge (the wave max of the lane maxima, each lane's sums rescaled to it
+//     once, fp64 sums by an xor butterfly 32, 16, 8, 4, 2, 1);
+//   * chunks: ((0,1),(2,3)),((4,5),(6,7)) by rlk_merge.
 // A vocab shard (split count S) owns 8/S consecutive chunks, reduces them in one
 // workgroup exactly as the unsplit case does, and hands its state to the merge kernel,
 // which applies the top S-leaf part of the same chunk tree.
@@ -296,26 +298,36 @@ void row_reduce_kernel(
       // reloaded right after it is folded (unrolled by two: no register copies).
       LaneFold fa = lane_fold_init(), fb = lane_fold_init();
       RawGroup<E> ra0, ra1, rb0, rb1;
-      if (A.n_groups > 0) issue_group(A.p, lane, 0, A.n, A.n_full, ra0);
-      if (B.n_groups > 0) issue_group(B.p, lane, 0, B.n, B.n_full, rb0);
-      if (A.n_groups > 1) issue_group(A.p, lane, 1, A.n, A.n_full, ra1);
-      if (B.n_groups > 1) issue_group(B.p, lane, 1, B.n, B.n_full, rb1);
       const int n = max(A.n_groups, B.n_groups);
       // Main loop: while both chunks' next groups are full, only wide loads are issued,
       // so every iteration issues the same loads in the same order and the compiler can
       // wait for exactly the group being folded (with the masked loads of a chunk's last
-      // group in the same loop it waited for every load in flight at each group).
+      // group in the same loop it waited for every load in flight at each group).  The
+      // loop is entered only from the first branch below, which issues the same four wide
+      // loads in the same order as an iteration does: a conditional or masked first load
+      // in front of the loop made the compiler wait for every load at the loop's head.
       const int n_full = min(A.n_full, B.n_full);
       int g = 0;
-      for (; g + 3 < n_full; g += 2) {
-        fold_raw(fa, ra0, c);
-        load_raw(A.p, lane, g + 2, ra0);
-        fold_raw(fb, rb0, c);
-        load_raw(B.p, lane, g + 2, rb0);
-        fold_raw(fa, ra1, c);
-        load_raw(A.p, lane, g + 3, ra1);
-        fold_raw(fb, rb1, c);
-        load_raw(B.p, lane, g + 3, rb1);
+      if (n_full >= 4) {
+        load_raw(A.p, lane, 0, ra0);
+        load_raw(B.p, lane, 0, rb0);
+        load_raw(A.p, lane, 1, ra1);
+        load_raw(B.p, lane, 1, rb1);
+        for (; g + 3 < n_full; g += 2) {
+          fold_raw(fa, ra0, c);
+          load_raw(A.p, lane, g + 2, ra0);
+          fold_raw(fb, rb0, c);
+          load_raw(B.p, lane, g + 2, rb0);
+          fold_raw(fa, ra1, c);
+          load_raw(A.p, lane, g + 3, ra1);
+          fold_raw(fb, rb1, c);
+          load_raw(B.p, lane, g + 3, rb1);
+        }
+      } else {
+        if (A.n_groups > 0) issue_group(A.p, lane, 0, A.n, A.n_full, ra0);
+        if (B.n_groups > 0) issue_group(B.p, lane, 0, B.n, B.n_full, rb0);
+        if (A.n_groups > 1) issue_group(A.p, lane, 1, A.n, A.n_full, ra1);
+        if (B.n_groups > 1) issue_group(B.p, lane, 1, B.n, B.n_full, rb1);
       }
       auto step = [&](int j, LaneFold& f, RawGroup<E>& r, const ChunkRef<E>& C) {
         if (j < C.n_groups) {
@@ -397,10 +409,10 @@ void row_reduce_kernel(
   }
 
   __shared__ State chunk_state[CPS];
-  sa = wave_tree(sa, c);
+  sa = wave_merge(sa, c);
   if (lane == 0) chunk_state[wave] = sa;
   if constexpr (CPW == 2) {
-    sb = wave_tree(sb, c);
+    sb = wave_merge(sb, c);
     if (lane == 0) chunk_state[wave + WAVES] = sb;
   }
   __syncthreads();

@@ -9,11 +9,12 @@
 //     logprob = (x_t - m) / tau - ln s,     entropy = ln s - ln(2) * u / s,
 // evaluated in fp64 (finalize) from the root state.
 //
-// Strictness: every merge in every kernel goes through rlk_merge() below, always with
-// the lower vocabulary range as its first operand, and the library is compiled with
-// -ffp-contract=off so that no compiler contraction changes a rounding.  Trees are
-// fixed functions of the vocabulary position only, never of the number of rows, the
-// row's place in a tile, the launch shape or the vocab split count.
+// Strictness: every merge of two states goes through rlk_merge() below, always with the
+// lower vocabulary range as its first operand; the one many-way merge, wave_merge() (the
+// 64 lane states of a logits-path chunk), is likewise one fixed function.  The library is
+// compiled with -ffp-contract=off so that no compiler contraction changes a rounding.
+// Trees are fixed functions of the vocabulary position only, never of the number of rows,
+// the row's place in a tile, the launch shape or the vocab split count.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -97,34 +98,6 @@ __device__ __forceinline__ WireState to_wire(const State& s, float xt) {
 // a = -inf) then adds nothing to u instead of 0 * (-inf) = NaN.  Otherwise equal to x * y.
 __device__ __attribute__((const, noconvergent)) float mul_zero_wins(float, float) __asm("llvm.amdgcn.fmul.legacy");
 
-// Leaf of 16 fp32 values v[0..15] (four quads of four): exact max m, then the fp32 terms
-// 2^a and 2^a * a with a = c (v - m) summed pairwise, within each quad and then across
-// quad pairs.  -inf entries contribute nothing; a leaf of only -inf is (-inf, 0, 0).
-__device__ __forceinline__ State leaf16(const float* v, float c) {
-  float mg = v[0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) mg = fmaxf(mg, v[i]);
-  const float mref = (mg == kNegInf) ? 0.0f : mg;
-  float e[16], t[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float a = (v[i] - mref) * c;
-    e[i] = exp2_hw(a);
-    t[i] = mul_zero_wins(e[i], a);
-  }
-  float sq[4], uq[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    sq[j] = (e[4 * j] + e[4 * j + 1]) + (e[4 * j + 2] + e[4 * j + 3]);
-    uq[j] = (t[4 * j] + t[4 * j + 1]) + (t[4 * j + 2] + t[4 * j + 3]);
-  }
-  State r;
-  r.m = mg;
-  r.s = (double)((sq[0] + sq[1]) + (sq[2] + sq[3]));
-  r.u = (double)((uq[0] + uq[1]) + (uq[2] + uq[3]));
-  return r;
-}
-
 // Wave-wide shuffle of a state (64 lanes).
 __device__ __forceinline__ State shfl_xor_state(const State& s, int mask) {
   State r;
@@ -134,17 +107,32 @@ __device__ __forceinline__ State shfl_xor_state(const State& s, int mask) {
   return r;
 }
 
-// Fixed xor-butterfly over the 64 lanes of a wave (strides 32, 16, 8, 4, 2, 1).  At each
-// level both partners evaluate the same merge with the lower lane's state first, so all
-// lanes end with identical bits.
-__device__ __forceinline__ State wave_tree(State st, float c) {
-  const int lane = threadIdx.x & 63;
+// The state of the union of a wave's 64 lane states, in one fixed order: the wave max M
+// of the lane maxima (exact, so its grouping does not matter), each lane's sums rescaled
+// to M once -- s 2^d and (u + d s) 2^d with d = c (m - M), one v_exp_f32, and 2^0 = 1
+// exactly for a lane at M -- then the fp64 sums over the lanes by an xor butterfly
+// (strides 32, 16, 8, 4, 2, 1).  Both partners of a butterfly step add the same two values,
+// so every lane ends with the same bits.  A lane of only -inf (m = -inf, s = u = 0) adds
+// 0; with M = -inf every lane is such a lane and the result is the identity; NaN in s or u
+// propagates, and a lane at M = +inf gets d = NaN, as rlk_merge gives it.  Against the
+// pairwise butterfly of rlk_merge this rounds each lane's contribution through one scale
+// factor instead of up to six, at a tenth of the instructions.
+__device__ __forceinline__ State wave_merge(const State& st, float c) {
+  float M = st.m;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  const float Mref = (M == kNegInf) ? 0.0f : M;
+  const float d = (st.m - Mref) * c;          // <= 0; -inf for a lane of only -inf
+  const double e = (double)exp2_hw(d);
+  const double dc = (double)fmaxf(d, -kMaxFloat);  // keeps 0 * (-inf) out of u
+  double s = st.s * e;
+  double u = fma(dc, st.s, st.u) * e;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
-    State o = shfl_xor_state(st, off);
-    st = (lane & off) ? rlk_merge(o, st, c) : rlk_merge(st, o, c);
+    s += __shfl_xor(s, off, 64);
+    u += __shfl_xor(u, off, 64);
   }
-  return st;
+  return State{M, s, u};
 }
 
 // Balanced tree over n = 1, 2, 4 or 8 consecutive states (lower index first):
