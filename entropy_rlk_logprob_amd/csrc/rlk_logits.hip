@@ -368,14 +368,19 @@ void row_reduce_kernel(
       const int n = A.n_groups;
       LaneFold f = lane_fold_init();
       RawGroup<E> r0, r1;
-      if (n > 0) issue_group(A.p, lane, 0, A.n, A.n_full, r0);
-      if (n > 1) issue_group(A.p, lane, 1, A.n, A.n_full, r1);
       int g = 0;
-      for (; g + 3 < A.n_full; g += 2) {  // wide loads only (see above)
-        fold_raw(f, r0, c);
-        load_raw(A.p, lane, g + 2, r0);
-        fold_raw(f, r1, c);
-        load_raw(A.p, lane, g + 3, r1);
+      if (A.n_full >= 4) {  // wide loads only, entered with its own loads in flight (see above)
+        load_raw(A.p, lane, 0, r0);
+        load_raw(A.p, lane, 1, r1);
+        for (; g + 3 < A.n_full; g += 2) {
+          fold_raw(f, r0, c);
+          load_raw(A.p, lane, g + 2, r0);
+          fold_raw(f, r1, c);
+          load_raw(A.p, lane, g + 3, r1);
+        }
+      } else {
+        if (n > 0) issue_group(A.p, lane, 0, A.n, A.n_full, r0);
+        if (n > 1) issue_group(A.p, lane, 1, A.n, A.n_full, r1);
       }
       for (; g < n; g += 2) {
         fold_raw(f, r0, c);
