@@ -114,7 +114,8 @@ __device__ __forceinline__ State shfl_xor_state(const State& s, int mask) {
 // (strides 32, 16, 8, 4, 2, 1).  Both partners of a butterfly step add the same two values,
 // so every lane ends with the same bits.  A lane of only -inf (m = -inf, s = u = 0) adds
 // 0; with M = -inf every lane is such a lane and the result is the identity; NaN in s or u
-// propagates, and a lane at M = +inf gets d = NaN, as rlk_merge gives it.  Against the
+// propagates.  A lane whose m is +inf has NaN sums already (its +inf term is NaN), and its
+// d = c (inf - inf) is NaN too, so M = +inf always yields NaN sums.  Against the
 // pairwise butterfly of rlk_merge this rounds each lane's contribution through one scale
 // factor instead of up to six, at a tenth of the instructions.
 __device__ __forceinline__ State wave_merge(const State& st, float c) {
