@@ -18,7 +18,7 @@ report (pr549, report.json) is "shared_logits_fp64" over all 1024 tokens of the 
 is that reference for the fused workloads: every row, logits as exact float64 dot products
 of the bf16 values.
 
-For the T=16384 workload it also stores selected rows of the fused backward's gradients
+For every fused workload it also stores selected rows of the fused backward's gradients
 (dH for 48 tokens, dW for 48 vocabulary rows, oracle.linear_grads_sampled) under seeded
 upstream gradients, with the magnitudes that bound their rounding.
 
@@ -145,7 +145,7 @@ def main():
     ap.add_argument("--rows-per-block", type=int, default=512)
     ap.add_argument("--only", type=int, choices=CFGS, default=None)
     ap.add_argument("--backward-only", action="store_true",
-                    help="only the T=16384 backward rows (needs its forward golden)")
+                    help="only the backward rows (needs the forward goldens)")
     args = ap.parse_args()
     manifest = {}
     if os.path.exists(MANIFEST):
@@ -164,8 +164,10 @@ def main():
         with open(MANIFEST, "w") as f:
             json.dump(manifest, f, indent=2)
             f.write("\n")
-    if args.only in (None, 5):
-        manifest["backward"][S.WORKLOADS[5].name] = make_backward(5)
+    for cfg in CFGS:
+        if args.only is not None and cfg != args.only:
+            continue
+        manifest["backward"][S.WORKLOADS[cfg].name] = make_backward(cfg)
         with open(MANIFEST, "w") as f:
             json.dump(manifest, f, indent=2)
             f.write("\n")

@@ -59,3 +59,51 @@ def test_goldens_match_a_fresh_oracle_evaluation():
     lp, ent = oracle.linear_logprob_entropy(h, w, case.targets[rows], wl.temperature)
     assert np.max(np.abs(lp - g["logprob"][rows])) <= 1e-12
     assert np.max(np.abs(ent - g["entropy"][rows])) <= 1e-12
+
+
+def _backward_golden(cfg):
+    import json
+    import os
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    with open(os.path.join(here, "fused_goldens.json")) as f:
+        meta = json.load(f)["backward"][S.WORKLOADS[cfg].name]
+    with np.load(os.path.join(here, meta["file"]), allow_pickle=False) as z:
+        return meta, {k: z[k] for k in z.files}
+
+
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_backward_goldens_are_complete(cfg):
+    """Every fused workload has its sampled backward rows: 48 dH rows and 48 dW rows of d
+    values, finite, with rounding magnitudes that dominate them, under the upstream
+    gradients the generator names (their sha256 must match)."""
+    wl = S.WORKLOADS[cfg]
+    meta, g = _backward_golden(cfg)
+    T, d, V = wl.n_tokens, wl.hidden, wl.vocab
+    assert meta["n_tokens"] == T
+    gl, ge = S.upstream_grads(cfg, T)
+    assert sha256(gl) == meta["sha256_g_logprob"] and sha256(ge) == meta["sha256_g_entropy"]
+    assert g["h_rows"].shape == (48,) and g["w_rows"].shape == (48,)
+    assert np.all((g["h_rows"] >= 0) & (g["h_rows"] < T))
+    assert np.all((g["w_rows"] >= 0) & (g["w_rows"] < V))
+    for k in ("dh", "dh_mag", "dw", "dw_mag"):
+        assert g[k].shape == (48, d) and np.all(np.isfinite(g[k])), k
+    assert np.all(np.abs(g["dh"]) <= g["dh_mag"] * (1 + 1e-12))
+    assert np.all(np.abs(g["dw"]) <= g["dw_mag"] * (1 + 1e-12))
+
+
+def test_backward_golden_dh_rows_match_a_fresh_oracle_evaluation():
+    """Two stored dH rows of the T=1024, d=2048 workload against the oracle's chain rule on
+    those rows alone: grad = oracle.logits_grad of the row's logits, dh = grad . W."""
+    wl = S.WORKLOADS[3]
+    _, g = _backward_golden(3)
+    fwd = load_fused_golden(wl.name)
+    case = S.fused_workload(3)
+    gl, ge = S.upstream_grads(3, wl.n_tokens)
+    sel = np.flatnonzero(gl[g["h_rows"]] != 0)[:2]  # two rows that are not masked
+    rows = g["h_rows"][sel]
+    assert len(rows) == 2
+    h = S.bf16_bits_to_f32(case.h_bits[rows]).astype(np.float64)
+    w = S.bf16_bits_to_f32(case.w_bits).astype(np.float64)
+    grad = oracle.logits_grad(h @ w.T, fwd["targets"][rows], wl.temperature, gl[rows], ge[rows])
+    dh = grad @ w
+    assert np.max(np.abs(dh - g["dh"][sel])) <= 1e-12 * max(1.0, np.abs(g["dh"][sel]).max())

@@ -239,15 +239,17 @@ def test_chunked_weight_gradient_continues_the_earlier_chunks(lib):
             np.all(dh_m[hi:] == 0)
 
 
-def test_large_ragged_batch_sampled_rows_vs_oracle(lib):
-    """T = 16384, d = 4096, V = 151936, tau = 0.7 with the golden targets and seeded upstream
-    gradients (every 7th row masked): 48 rows of dH and 48 rows of dW against the fp64 oracle
-    (tests/golden, oracle.linear_grads_sampled) within the bf16-rounding + fp32-accumulation
-    bound; vocab split 4 bitwise equal to split 1.  The workspace is that of one 4096-token
-    chunk (the call runs four)."""
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_fused_workload_backward_sampled_rows_vs_oracle(lib, cfg):
+    """Each fused workload (T = 1024 / d = 2048; T = 2048 / d = 4096; T = 16384 / d = 4096,
+    tau = 0.7, the golden targets) with seeded upstream gradients (every 7th row masked):
+    48 rows of dH and 48 rows of dW against the fp64 oracle (tests/golden,
+    oracle.linear_grads_sampled) within the bf16-rounding + fp32-accumulation bound, and
+    vocab split 4 bitwise equal to split 1.  At T = 16384 the workspace is that of one
+    4096-token chunk (the call runs four)."""
     import torch
     from tests.helpers import load_fused_golden
-    wl = S.WORKLOADS[5]
+    wl = S.WORKLOADS[cfg]
     fwd = load_fused_golden(wl.name)
     import json
     import os
@@ -257,16 +259,18 @@ def test_large_ragged_batch_sampled_rows_vs_oracle(lib):
     with np.load(os.path.join(here, meta["file"]), allow_pickle=False) as z:
         g = {k: z[k] for k in z.files}
     announce(f"generating fused workload {wl.name} (backward)")
-    case = S.fused_workload(5)
+    case = S.fused_workload(cfg)
     T, d = case.h_bits.shape
     V = case.w_bits.shape[0]
-    gl, ge = S.upstream_grads(5, T)
-    assert lib.workspace_bytes(B.OP_LINEAR_BACKWARD, T, V, d, 1) == \
-        lib.workspace_bytes(B.OP_LINEAR_BACKWARD, 4096, V, d, 1)
+    tau = wl.temperature
+    gl, ge = S.upstream_grads(cfg, T)
+    if T > 4096:
+        assert lib.workspace_bytes(B.OP_LINEAR_BACKWARD, T, V, d, 1) == \
+            lib.workspace_bytes(B.OP_LINEAR_BACKWARD, 4096, V, d, 1)
     hd, wd, td = bits_dev(case.h_bits), bits_dev(case.w_bits), dev(fwd["targets"])
     gld, ged = dev(gl), dev(ge)
-    announce("linear backward T=16384 split=1")
-    dh, dw = lib.linear_logprob_backward(hd, wd, td, 0.7, 1, gld, ged)
+    announce(f"linear backward T={T} d={d} split=1")
+    dh, dw = lib.linear_logprob_backward(hd, wd, td, tau, 1, gld, ged)
     torch.cuda.synchronize()
     hr, wr = torch.from_numpy(g["h_rows"]).cuda(), torch.from_numpy(g["w_rows"]).cuda()
     dh_s, dw_s = dh[hr].cpu().numpy(), dw[wr].cpu().numpy()
@@ -275,12 +279,12 @@ def test_large_ragged_batch_sampled_rows_vs_oracle(lib):
     check(dw_s, g["dw"], (2.0 ** -8 + Tp * 2.0 ** -24) * g["dw_mag"] + 1e-30)
     rel_dh = np.abs(dh_s - g["dh"]).max() / np.abs(g["dh"]).max()
     rel_dw = np.abs(dw_s - g["dw"]).max() / np.abs(g["dw"]).max()
-    print(f"[T=16384 backward] max |err| / max |ref|: dH {rel_dh:.2e}, dW {rel_dw:.2e}",
+    print(f"[T={T} d={d} backward] max |err| / max |ref|: dH {rel_dh:.2e}, dW {rel_dw:.2e}",
           flush=True)
     masked = np.flatnonzero((gl[g["h_rows"]] == 0) & (ge[g["h_rows"]] == 0))
     assert masked.size > 0 and np.all(dh_s[masked] == 0)
-    announce("linear backward T=16384 split=4")
-    dh4, dw4 = lib.linear_logprob_backward(hd, wd, td, 0.7, 4, gld, ged)
+    announce(f"linear backward T={T} d={d} split=4")
+    dh4, dw4 = lib.linear_logprob_backward(hd, wd, td, tau, 4, gld, ged)
     torch.cuda.synchronize()
     assert torch.equal(dh4.view(torch.int32), dh.view(torch.int32))
     assert torch.equal(dw4.view(torch.int32), dw.view(torch.int32))
