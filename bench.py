@@ -477,7 +477,7 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "fused": fused,
         "fused_backward": fused_backward, "splits_ms": splits,
         "bf16_logits": bf16, "backward": backward, "ceilings": ceilings,
-        "device": torch.cuda.get_device_name(0),
+        "device": dict(name=torch.cuda.get_device_name(0), **probes.device_info()),
     }
     print(json.dumps(out), flush=True)
 

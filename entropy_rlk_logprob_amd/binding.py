@@ -502,6 +502,9 @@ class Probes:
         self.lib.rlk_probe_stream_read.restype = ctypes.c_int
         self.lib.rlk_probe_mfma.argtypes = [i32, i32, u32, vp, vp]
         self.lib.rlk_probe_mfma.restype = ctypes.c_int
+        pi32 = ctypes.POINTER(ctypes.c_int32)
+        self.lib.rlk_probe_device_info.argtypes = [pi32, pi32, pi32, pi32, ctypes.c_char_p, sz]
+        self.lib.rlk_probe_device_info.restype = ctypes.c_int
 
     @staticmethod
     def _stream(dev):
@@ -519,6 +522,20 @@ class Probes:
         if st != 0:
             raise RuntimeError(f"rlk_probe_stream_read failed ({st})")
         return nbytes
+
+    def device_info(self) -> dict:
+        """rlk_probe_device_info of the current device, with the dense bf16 MFMA peak it implies
+        (compute units x engine clock x 4096 flop per clock)."""
+        cu, clk, mclk, bus = (ctypes.c_int32() for _ in range(4))
+        arch = ctypes.create_string_buffer(64)
+        st = self.lib.rlk_probe_device_info(ctypes.byref(cu), ctypes.byref(clk), ctypes.byref(mclk),
+                                            ctypes.byref(bus), arch, len(arch))
+        if st != 0:
+            raise RuntimeError(f"rlk_probe_device_info failed ({st})")
+        return {"arch": arch.value.decode(), "compute_units": cu.value,
+                "engine_clock_mhz": clk.value / 1e3, "memory_clock_mhz": mclk.value / 1e3,
+                "memory_bus_bits": bus.value,
+                "mfma_bf16_dense_peak_tflops": round(cu.value * clk.value * 1e3 * 4096 / 1e12, 1)}
 
     def mfma(self, blocks: int, iters: int, sink, seed: int = 1):
         """Returns the flops of one launch; sink: >= blocks * 256 floats."""

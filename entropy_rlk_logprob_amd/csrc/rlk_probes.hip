@@ -3,6 +3,8 @@
 // can state each kernel's rate against what is achievable as well as against the peak.
 
 #include <hip/hip_runtime.h>
+
+#include <cstring>
 #include <stdint.h>
 
 #include "rlk_probes.h"
@@ -99,6 +101,27 @@ int rlk_probe_mfma(int32_t blocks, int32_t iters, uint32_t seed, float* sink, vo
   hipLaunchKernelGGL(mfma_probe_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), iters, seed, sink);
   return (int)hipGetLastError();
+}
+
+int rlk_probe_device_info(int32_t* compute_units, int32_t* engine_clock_khz,
+                          int32_t* memory_clock_khz, int32_t* memory_bus_bits, char* arch,
+                          size_t arch_len) {
+  if (!compute_units || !engine_clock_khz || !memory_clock_khz || !memory_bus_bits || !arch ||
+      arch_len == 0)
+    return -1;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return (int)e;
+  *compute_units = prop.multiProcessorCount;
+  *engine_clock_khz = prop.clockRate;
+  *memory_clock_khz = prop.memoryClockRate;
+  *memory_bus_bits = prop.memoryBusWidth;
+  std::strncpy(arch, prop.gcnArchName, arch_len - 1);
+  arch[arch_len - 1] = '\0';
+  return 0;
 }
 
 }  // extern "C"

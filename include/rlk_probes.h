@@ -34,6 +34,15 @@ int rlk_probe_stream_read(const void* buf, size_t bytes, float* sink, void* stre
  * Work = blocks * 4 * iters * 8 * 32768 flop. */
 int rlk_probe_mfma(int32_t blocks, int32_t iters, uint32_t seed, float* sink, void* stream);
 
+/* Properties of the current device behind the peak figures (host only, launches nothing):
+ * the compute-unit count, the peak engine clock and the memory clock in kHz, the memory bus
+ * width in bits, and the architecture name (NUL-terminated, truncated to arch_len - 1).  The
+ * dense bf16 MFMA peak is compute_units x engine clock x 4096 flop per clock.  Returns 0, a
+ * hipError_t value if the query fails, or -1 for a null pointer. */
+int rlk_probe_device_info(int32_t* compute_units, int32_t* engine_clock_khz,
+                          int32_t* memory_clock_khz, int32_t* memory_bus_bits, char* arch,
+                          size_t arch_len);
+
 #ifdef __cplusplus
 }
 #endif

@@ -48,7 +48,7 @@ def test_probe_library_exports_its_header():
     """librlk_probes.so (the benchmark's measurement probes) exports what
     include/rlk_probes.h declares and rejects bad arguments without launching."""
     names = B.header_functions(B.PROBES_HEADER)
-    assert set(names) == {"rlk_probe_stream_read", "rlk_probe_mfma"}
+    assert set(names) == {"rlk_probe_stream_read", "rlk_probe_mfma", "rlk_probe_device_info"}
     P = B.load_probes()
     for n in names:
         assert ctypes.cast(getattr(P.lib, n), ctypes.c_void_p).value
@@ -59,6 +59,11 @@ def test_probe_library_exports_its_header():
     assert P.lib.rlk_probe_mfma(0, 4, 1, vp(FAKE), None) == -1
     assert P.lib.rlk_probe_mfma(1, 6, 1, vp(FAKE), None) == -1                    # iters % 4
     assert P.lib.rlk_probe_mfma(1, 4, 1, None, None) == -1
+    i32 = ctypes.c_int32()
+    assert P.lib.rlk_probe_device_info(None, ctypes.byref(i32), ctypes.byref(i32),
+                                       ctypes.byref(i32), ctypes.create_string_buffer(8), 8) == -1
+    assert P.lib.rlk_probe_device_info(ctypes.byref(i32), ctypes.byref(i32), ctypes.byref(i32),
+                                       ctypes.byref(i32), ctypes.create_string_buffer(8), 0) == -1
 
 
 def test_backend_and_status_strings(L):
