@@ -150,20 +150,17 @@ __global__ __launch_bounds__(kThreads, 1) void dx_tile_kernel(
   // of rows v_lo + wv 128 + a 32 + 8 g4 + 4 fhalf + j (a, g4, j = 0..3) in acc[a][b][4 g4 + j].
   const int64_t row0 = v_lo + wv * 128 + 4 * fhalf;  // this lane's first row
   if (v_lo + kTile <= V && t_lo + kTile <= T) {
-    // Full tile: no bounds tests.  dX rows are stored 8 bytes (4 rows) at a time from a
-    // per-lane base with immediate offsets.  A dX^T element of row row0 + off + j sits at the
-    // wave-uniform base of row v_lo + wv 128 + off (scalar registers) plus a per-lane 32-bit
-    // byte offset, one per j, fixed for the token.
+    // Full tile: the bf16 gradient tile (128 KiB) goes through the LDS, which the K loop no
+    // longer needs, once per layout, so that dX and dX^T are both written with 16-byte stores
+    // whose 32 lanes cover 512 contiguous bytes of a row (four whole 128-byte lines).  Written
+    // straight from the MFMA layout, dX took 8-byte stores that touch 32 lines each and dX^T
+    // 2-byte stores, and the tile's stores cost several times its MFMAs' last steps.
+    uint32_t w[2][4][4][2];  // token b; rows row0 + a 32 + 8 g4 + {0,1} and {2,3}, packed
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int64_t tok = t_lo + wt * 64 + b * 32 + frow;
       const GradRowC r = rc[tok];
       const int tgt = (r.t >= row0 && r.t < row0 + 128) ? (int)(r.t - row0) : -1;
-      uint16_t* const xrow = dX ? dX + tok * ldx + row0 : nullptr;
-      uint32_t xt_off[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        xt_off[j] = (uint32_t)(((4 * fhalf + j) * ldxt + (tok - t_lo)) * 2);
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
 #pragma unroll
@@ -172,16 +169,67 @@ __global__ __launch_bounds__(kThreads, 1) void dx_tile_kernel(
           float g[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) g[j] = logit_grad(acc[a][b][4 * g4 + j], tgt == off + j, r, c);
-          const uint32_t w0 = pack_bf16(g[0], g[1]), w1 = pack_bf16(g[2], g[3]);
-          if (dX) *reinterpret_cast<uint2*>(xrow + off) = make_uint2(w0, w1);
-          if (dXT) {
-            char* rb = reinterpret_cast<char*>(dXT + (v_lo + wv * 128 + off) * ldxt + t_lo);
-            const uint16_t h[4] = {(uint16_t)w0, (uint16_t)(w0 >> 16), (uint16_t)w1,
-                                   (uint16_t)(w1 >> 16)};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) *reinterpret_cast<uint16_t*>(rb + xt_off[j]) = h[j];
-          }
+          w[b][a][g4][0] = pack_bf16(g[0], g[1]);
+          w[b][a][g4][1] = pack_bf16(g[2], g[3]);
         }
+      }
+    }
+    // LDS tile: 256 rows of 512 bytes (32 16-byte columns).  dX: row = token, column c of a
+    // row at c ^ (row % 32); dX^T: row = vocabulary row, column c at c ^ 4 ((row / 4) % 8).
+    // Both keep the 32 lanes of a write or read instruction off each other's banks.
+    char* const tile = smem;
+    const int wvrow = wv * 128 + 4 * fhalf;  // this lane's first vocabulary row in the tile
+    if (dX) {
+      __syncthreads();  // every wave is done with the K loop's stages (or the last dX^T pass)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int tl = wt * 64 + b * 32 + frow;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int vl = wvrow + a * 32 + 8 * g4;  // 4 rows: bytes 2 vl .. 2 vl + 7
+            *reinterpret_cast<uint2*>(tile + tl * 512 + (((vl >> 3) ^ (tl & 31)) << 4) +
+                                      ((vl & 4) << 1)) =
+                make_uint2(w[b][a][g4][0], w[b][a][g4][1]);
+          }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tl = wave * 32 + 2 * i + (lane >> 5);
+        const int col = lane & 31;
+        const uint4 q = *reinterpret_cast<const uint4*>(tile + tl * 512 + ((col ^ (tl & 31)) << 4));
+        *reinterpret_cast<uint4*>(dX + (t_lo + tl) * ldx + v_lo + 8 * col) = q;
+      }
+    }
+    if (dXT) {
+      __syncthreads();
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int tl = wt * 64 + b * 32 + frow;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int vl = wvrow + a * 32 + 8 * g4 + j;
+              const uint32_t word = w[b][a][g4][j >> 1];
+              *reinterpret_cast<uint16_t*>(tile + vl * 512 +
+                                           (((tl >> 3) ^ (4 * ((vl >> 2) & 7))) << 4) +
+                                           ((tl & 7) << 1)) =
+                  (uint16_t)((j & 1) ? (word >> 16) : word);
+            }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int vl = wave * 32 + 2 * i + (lane >> 5);
+        const int col = lane & 31;
+        const uint4 q = *reinterpret_cast<const uint4*>(
+            tile + vl * 512 + ((col ^ (4 * ((vl >> 2) & 7))) << 4));
+        *reinterpret_cast<uint4*>(dXT + (v_lo + vl) * ldxt + t_lo + 8 * col) = q;
       }
     }
     return;
