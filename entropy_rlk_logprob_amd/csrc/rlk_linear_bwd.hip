@@ -350,9 +350,13 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, in
 // clamped, the other operand holding zeros there).  Stored row-major at C[m * ldc + n]
 // (32 lanes write 128 contiguous bytes of a row).  Split s (blockIdx.y) covers K steps
 // [s * steps, (s + 1) * steps) and writes C + s * split_stride; an empty range writes 0.
-// Tile order (tile_of): SHARE_B groups row tiles and runs column-tile-major within a group
-// (consecutive logical tiles share a B slice), else the reverse (they share an A slice):
-// the larger operand is fetched from HBM once and shared in an XCD's L2.
+// Tile order: SHARE_B groups row tiles by 4 and runs column-tile-major within a group
+// (consecutive logical tiles share a B slice), else the reverse with groups of 8 (they share
+// an A slice): the larger operand is fetched from HBM once and shared in an XCD's L2.  For
+// dH (SHARE_B) each XCD then takes 4 W column tiles x 4 token tiles of a K range instead of
+// 2 x 8, so that each XCD no longer reads the whole token range of dX: 6.994-6.998 ms against
+// 7.005-7.013 ms for the whole backward at T = 2048, d = 4096, V = 151936 (groups of 2:
+// 7.028-7.030 ms).
 template <bool A_KMAJOR, bool B_KMAJOR, bool SHARE_B, bool ACCUM = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const uint16_t* __restrict__ A, int64_t lda, int64_t M, int64_t a_klast,
@@ -361,7 +365,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
   int64_t mt, nt;
   const int64_t n_mt = (M + kTile - 1) / kTile, n_nt = (N + kTile - 1) / kTile;
-  if (!(SHARE_B ? tile_of(n_nt, n_mt, nt, mt) : tile_of(n_mt, n_nt, mt, nt))) return;
+  if (!(SHARE_B ? mma::grouped_tile_of<4>(n_nt, n_mt, nt, mt) : tile_of(n_mt, n_nt, mt, nt)))
+    return;
   const int64_t m_lo = mt * kTile, n_lo = nt * kTile;
   const int64_t k_begin = (int64_t)blockIdx.y * steps * kBK;
   const int64_t k_end = min(k_begin + steps * kBK, K);
