@@ -95,16 +95,17 @@ __device__ __forceinline__ State leaf64(const float (&v)[4][16], float c) {
   return r;
 }
 
-template <bool WITH_U>
+// G: token tiles per group of the tile order (see grouped_tile_of and launch_linear_path).
+template <bool WITH_U, int G = 8>
 __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
     const uint16_t* __restrict__ H, int64_t ldh, const uint16_t* __restrict__ W, int64_t ldw,
     int64_t d, TileGeom g, const int64_t* __restrict__ targets, float c,
     WireState* __restrict__ tile_states, float* __restrict__ target_logit) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
 
-  // Vocabulary tiles x token tiles, token tiles in groups of 8 (see grouped_tile_of).
+  // Vocabulary tiles x token tiles, token tiles in groups of G (see grouped_tile_of).
   int64_t vt, tt;
-  if (!mma::grouped_tile_of<8>(g.n_vt, g.n_tt, vt, tt)) return;
+  if (!mma::grouped_tile_of<G>(g.n_vt, g.n_tt, vt, tt)) return;
   const int64_t chunk = vt / g.tpc;
   const int64_t kin = vt % g.tpc;
   const int64_t chunk_lo = min(chunk * g.Vc, g.V);
@@ -515,16 +516,25 @@ hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream) {
                          a.W, a.ldw, a.d, g, a.targets, a.c,
                          reinterpret_cast<WireState*>(base + L.tile_states),
                          reinterpret_cast<float*>(base + L.target_logit));
-  } else if (with_u)
-    hipLaunchKernelGGL(linear_tile_kernel<true>, split_grid(nb_pad), dim3(kThreads), 0, stream,
-                       a.H, a.ldh, a.W, a.ldw, a.d, g, a.targets, a.c,
-                       reinterpret_cast<WireState*>(base + L.tile_states),
-                       reinterpret_cast<float*>(base + L.target_logit));
-  else
-    hipLaunchKernelGGL(linear_tile_kernel<false>, split_grid(nb_pad), dim3(kThreads), 0, stream,
-                       a.H, a.ldh, a.W, a.ldw, a.d, g, a.targets, a.c,
-                       reinterpret_cast<WireState*>(base + L.tile_states),
-                       reinterpret_cast<float*>(base + L.target_logit));
+  } else {
+    // Token tiles per group of the tile order: an XCD runs ~32 tiles at once, i.e. a few
+    // vocabulary tiles times one group.  With 5 to 8 token tiles (1024 < T <= 2048), groups
+    // of 4 (8 vocabulary tiles at once, H of 4 token tiles re-read from the infinity cache
+    // every 8 vocabulary tiles, W read by two XCDs) measured +0.2 to +0.5 points at T = 2048
+    // over one group of 8 (three same-process A/Bs on three boxes, bits equal); with up to 4 token tiles both give
+    // one group, and with more than 8, groups of 8 (T = 16384: 51.9% against 51.0% with 4).
+    auto launch = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, split_grid(nb_pad), dim3(kThreads), 0, stream, a.H, a.ldh, a.W,
+                         a.ldw, a.d, g, a.targets, a.c,
+                         reinterpret_cast<WireState*>(base + L.tile_states),
+                         reinterpret_cast<float*>(base + L.target_logit));
+    };
+    const bool g4 = g.n_tt > 4 && g.n_tt <= 8;
+    if (with_u)
+      g4 ? launch(linear_tile_kernel<true, 4>) : launch(linear_tile_kernel<true, 8>);
+    else
+      g4 ? launch(linear_tile_kernel<false, 4>) : launch(linear_tile_kernel<false, 8>);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
