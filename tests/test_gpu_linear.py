@@ -104,13 +104,15 @@ def test_paired_tiles_match_full_tiles(lib, V):
     assert max_abs(lp, olp) <= TOL_LINEAR and max_abs(ent, oent) <= TOL_LINEAR
 
 
-def test_token_tile_groups_with_partial_last_group(lib):
+@pytest.mark.parametrize("T,group", [(2600, 8), (1300, 4)])
+def test_token_tile_groups_with_partial_last_group(lib, T, group):
     """T = 2600: 11 token tiles, which the kernel runs as a group of 8 and a partial group
-    of 3.  Every row against the oracle; the rows of the partial group alone, and vocab
-    split 4, give the same bits."""
-    T, d, V = 2600, 64, 3000
-    announce(f"linear T={T} d={d} V={V} (token tile groups 8 + 3)")
-    case = S.random_fused_case(T, d, V, seed=9100, h_sigma=1.0, w_sigma=3.0 / math.sqrt(d))
+    of 3; T = 1300: 6 token tiles, run in groups of 4 (the order for 5 to 8 token tiles) as
+    4 + 2.  Every row against the oracle; the rows of the partial group alone (run in the
+    order for their own count of token tiles), and vocab split 4, give the same bits."""
+    d, V = 64, 3000
+    announce(f"linear T={T} d={d} V={V} (token tile groups of {group}, partial last group)")
+    case = S.random_fused_case(T, d, V, seed=9100 + T, h_sigma=1.0, w_sigma=3.0 / math.sqrt(d))
     olp, oent = oracle.linear_logprob_entropy(f32(case.h_bits), f32(case.w_bits), case.targets,
                                               1.0)
     h, w, t = bits_dev(case.h_bits), bits_dev(case.w_bits), dev(case.targets)
@@ -118,7 +120,7 @@ def test_token_tile_groups_with_partial_last_group(lib):
     assert max_abs(lp, olp) <= TOL_LINEAR and max_abs(ent, oent) <= TOL_LINEAR
     lp4, ent4 = run_linear(lib, h, w, t, 1.0, 4)
     assert bitwise_equal(lp4, lp) and bitwise_equal(ent4, ent)
-    lo = 8 * 256
+    lo = group * 256
     lpt, entt = run_linear(lib, h[lo:], w, t[lo:])
     assert bitwise_equal(lpt, lp[lo:]) and bitwise_equal(entt, ent[lo:])
 
