@@ -20,7 +20,9 @@ Also reported on the same JSON line:
                 oracle's tempered softmax as stored with the parity goldens), each with its
                 fraction next to the 50% target; fused.logprob_only times the same call
                 without the entropy output; fused.cpu_baseline times the oracle on every
-                row of the T = 1024, d = 2048 shape;
+                row of the T = 1024, d = 2048 shape; fused.configs[*].vendor_gemm times
+                the same 2 T V d flops as one plain torch.mm H W^T (hipBLASLt) with bf16
+                and with fp32 logits out, for context (no softmax epilogue, logits written);
   splits        ms per call of the logits path at vocab splits 2, 4, 8;
   bf16_logits   the same rows rounded to bf16 through rlk_logprob_from_logits_bf16
                 (1024 x 303888 B per call) as GB/s against 8 TB/s;
@@ -133,8 +135,28 @@ def fused_config_rate(lib, h, w, t, tau, steps, warmup):
     ms, _ = time_calls(lambda: lib.linear_logprob(h, w, t, tau, 1, out=(lp, ent), workspace=ws),
                        steps, warmup)
     tf = 2.0 * T * V * d / (ms / 1e3) / 1e12
+    del ws
+    log(f"timing torch.mm (hipBLASLt) T={T} d={d}")
     return {"n_tokens": T, "hidden": d, "temperature": tau, "ms_per_call": round(ms, 4),
-            "tokens_per_s": round(T / (ms / 1e3), 1), "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+            "tokens_per_s": round(T / (ms / 1e3), 1), "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "vendor_gemm": vendor_gemm_rate(h, w, min(steps, 5), 3)}
+
+
+def vendor_gemm_rate(h, w, steps, warmup):
+    """The same 2 T V d flops as one plain GEMM H W^T through torch.mm (hipBLASLt), with the
+    logits written out in bf16 and in fp32: context for the fused path's fraction of peak (the
+    library GEMM has no softmax epilogue, but it writes T x V logits).  h, w: bf16 bits."""
+    import torch
+    hb, wb = h.view(torch.bfloat16), w.view(torch.bfloat16)
+    T, d = hb.shape
+    V = wb.shape[0]
+    out = {}
+    for name, dt in (("bf16_out", torch.bfloat16), ("fp32_out", torch.float32)):
+        ms, _ = time_calls(lambda dt=dt: torch.mm(hb, wb.t(), out_dtype=dt), steps, warmup)
+        tf = 2.0 * T * V * d / (ms / 1e3) / 1e12
+        out[name] = {"ms_per_call": round(ms, 4), "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+    torch.cuda.empty_cache()
+    return out
 
 
 def host_description() -> dict:
@@ -428,8 +450,10 @@ def main():
                      "waves per CU"}
         fused["roofline"]["frac_of_probe"] = round(tflops / mtf, 4)
         fused_backward["roofline"]["frac_of_probe"] = round(btf / mtf, 4)
+        log("timing torch.mm (hipBLASLt) T=2048 d=4096")
         fused_configs = {S.WORKLOADS[4].name: {"ms_per_call": fused["ms_per_call"],
-                                               "frac": fused["roofline"]["frac"]}}
+                                               "frac": fused["roofline"]["frac"],
+                                               "vendor_gemm": vendor_gemm_rate(h, w, 5, 3)}}
         if not args.no_fused_configs:
             del w
             # The large ragged batch with its own inputs: H and W from its seed, and the
