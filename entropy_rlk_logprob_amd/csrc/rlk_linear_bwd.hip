@@ -16,8 +16,8 @@
 //      [V, Tp] (for dW), with zero K padding;
 //   4. dH = dX . W on the shared tile loop, dX K-contiguous and W read in place as a
 //      K-major operand (gfx950 LDS transpose loads, so no transposed copy of W is made);
-//      K = Vp split into 8 fixed ranges (boundaries depend on V only), partials summed in
-//      the fixed tree ((0,1),(2,3)),((4,5),(6,7));
+//      K = Vp split into 4 fixed ranges (boundaries depend on V only), partials summed in
+//      the fixed tree (0,1),(2,3);
 //   5. dW = dX^T . H with dX^T and a transposed copy of H (small), K = Tp in one
 //      increasing-order pass per output tile.
 // A token's row of dH depends only on that token (its place among the GEMM's columns does
@@ -40,7 +40,10 @@ using mma::kStageBytes;
 using mma::kThreads;
 
 constexpr int kTile = 256;
-constexpr int kDhSplits = 8;
+// Fixed K ranges of dH.  4 against 8: half the fp32 partials (134 against 268 MB at
+// T = 2048, d = 4096) and half the per-job fixed costs, in 2 rounds of 512 jobs instead of 4 of
+// 1024 on 256 CUs: the whole backward 0.8% faster at that shape (same-process A/B, 3 of 3).
+constexpr int kDhSplits = 4;
 
 // Per-token constants of the logit gradient: the root state's m and log2 s, the entropy H,
 // the upstream gradients times 1/tau (bgl, bge), the row mode and the value a row that is
@@ -425,8 +428,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   }
 }
 
-// out[t, k] = ((P0 + P1) + (P2 + P3)) + ((P4 + P5) + (P6 + P7)), P_s = part + s * stride,
-// part rows of d floats; 4 consecutive k per thread (d is a multiple of 64).
+// out[t, k] = (P0 + P1) + (P2 + P3), P_s = part + s * stride, part rows of d floats; 4
+// consecutive k per thread (d is a multiple of 64).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                             int64_t stride, int64_t T, int64_t d,
                                                             float* __restrict__ out, int64_t ldo) {
@@ -439,7 +442,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   for (int s = 0; s < kDhSplits; ++s)
     v[s] = *reinterpret_cast<const float4*>(part + s * stride + t * d + k);
   auto add = [](float4 x, float4 y) { return make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w); };
-  const float4 r = add(add(add(v[0], v[1]), add(v[2], v[3])), add(add(v[4], v[5]), add(v[6], v[7])));
+  static_assert(kDhSplits == 4, "the reduction tree below");
+  const float4 r = add(add(v[0], v[1]), add(v[2], v[3]));
   float* dst = out + t * ldo + k;
   dst[0] = r.x;
   dst[1] = r.y;

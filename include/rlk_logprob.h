@@ -283,7 +283,7 @@ rlk_status rlk_logprob_backward_from_logits(const float* logits, int64_t ld_logi
  * rlk_logprob_backward_from_logits:   grad_hidden = dX . weight,   grad_weight = dX^T . hidden.
  * The RL-Kernel h100-pcp.json evidence page's training records consume both outputs and
  * find the trained weights equal across parallel configurations: the reductions here have
- * fixed orders (the vocabulary in 8 fixed ranges summed in a fixed tree for grad_hidden,
+ * fixed orders (the vocabulary in 4 fixed ranges summed in a fixed tree for grad_hidden,
  * the tokens in increasing order for grad_weight), with no atomics, so results repeat
  * bitwise, and each row of grad_hidden is independent of the other rows of the batch.
  *   hidden, ld_hidden, weight, ld_weight, n_tokens, hidden_dim, vocab, target_ids,
