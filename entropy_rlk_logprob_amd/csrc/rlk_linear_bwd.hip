@@ -130,7 +130,13 @@ __global__ __launch_bounds__(kThreads, 1) void dx_tile_kernel(
     uint16_t* __restrict__ dX, int64_t ldx, uint16_t* __restrict__ dXT, int64_t ldxt) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
   int64_t vt, tt;
-  if (!tile_of((V + kTile - 1) / kTile, (T + kTile - 1) / kTile, vt, tt)) return;
+  // Tile order as in the forward, which runs the same tile loop: with 5 to 8 token tiles, groups
+  // of 4 token tiles (0.1-0.5% faster for the whole backward at T = 2048 in a same-process A/B,
+  // 3 of 3, bits equal), else of 8.
+  const int64_t n_vt = (V + kTile - 1) / kTile, n_tt = (T + kTile - 1) / kTile;
+  if (!((n_tt > 4 && n_tt <= 8) ? mma::grouped_tile_of<4>(n_vt, n_tt, vt, tt)
+                                : tile_of(n_vt, n_tt, vt, tt)))
+    return;
   const int64_t v_lo = vt * kTile;
   const int64_t t_lo = tt * kTile;
   const int n_v = (int)min((int64_t)kTile, V - v_lo);
