@@ -228,11 +228,12 @@ __device__ __forceinline__ void fold_raw(LaneFold& f, const RawGroup<E>& r, floa
   fold_group(f, v.v, c);
 }
 
-// Chunks per wave for a shard of CPS chunks.  fp32 logits: one (8192 waves for 1024 rows,
-// all resident at eight waves per SIMD, the most bytes in flight for an HBM-bound stream).
-// bf16 logits, which are bound by VALU issue: two when the shard has two or more (4096
-// waves, one round at four or more per SIMD), which leaves the registers to unroll the
-// double buffer so that no register copies are issued per group -- 6% faster.
+// Chunks per wave for a shard of CPS chunks.  fp32 logits: one (8192 waves for 1024 rows),
+// of which 4096 are resident at a time (four per SIMD, capped by rows_resident_lds), each
+// with two groups in flight.  bf16 logits, which are bound by VALU issue: two when the shard
+// has two or more (4096 waves, one round at four or more per SIMD), which leaves the
+// registers to unroll the double buffer so that no register copies are issued per group --
+// 6% faster.
 template <typename E>
 constexpr int chunks_per_wave(int cps) { return (sizeof(E) == 2 && cps >= 2) ? 2 : 1; }
 template <typename E>
@@ -264,7 +265,7 @@ __device__ __forceinline__ ChunkRef<E> chunk_ref(const E* row_base, int64_t chun
 // wave folds a chunk does not change its bits.
 template <typename E, int CPS, bool VEC>
 __global__ __launch_bounds__(64 * waves_for<E>(CPS))
-__attribute__((amdgpu_waves_per_eu(chunks_per_wave<E>(CPS) == 2 ? 4 : 8)))
+__attribute__((amdgpu_waves_per_eu((chunks_per_wave<E>(CPS) == 2 || sizeof(E) == 4) ? 4 : 8)))
 void row_reduce_kernel(
     const E* __restrict__ X, int64_t ld, int64_t T, int64_t V, int64_t Vc,
     const int64_t* __restrict__ targets, float c, double beta, float* __restrict__ lp_out,
@@ -343,28 +344,10 @@ void row_reduce_kernel(
       }
       sa = fa.st;
       sb = fb.st;
-    } else if constexpr (sizeof(E) == 4) {
-      // fp32, eight waves per SIMD within 64 VGPRs: the next group in flight while a group
-      // is folded (a second buffer pair would spill).
-      const int n = A.n_groups;
-      LaneFold f = lane_fold_init();
-      RawGroup<E> cur, nxt;
-      if (n > 0) issue_group(A.p, lane, 0, A.n, A.n_full, cur);
-      int j = 0;
-      for (; j + 1 < A.n_full; ++j) {  // next group full: wide loads only (see above)
-        load_raw(A.p, lane, j + 1, nxt);
-        fold_raw(f, cur, c);
-        cur = nxt;
-      }
-      for (; j < n; ++j) {
-        if (j + 1 < n) issue_group(A.p, lane, j + 1, A.n, A.n_full, nxt);
-        fold_raw(f, cur, c);
-        cur = nxt;
-      }
-      sa = f.st;
     } else {
       // One chunk through two buffers (unrolled by two: no register copies), the next two
-      // groups in flight while a group is folded.
+      // groups in flight while a group is folded.  fp32 runs here at four waves per SIMD (see
+      // rows_resident): fewer concurrent streams over the logits, each with two groups in flight.
       const int n = A.n_groups;
       LaneFold f = lane_fold_init();
       RawGroup<E> r0, r1;
@@ -464,12 +447,29 @@ __global__ __launch_bounds__(256) void shard_merge_kernel(
                  ent_out ? ent_out + row : nullptr);
 }
 
+// fp32 logits: dynamic LDS that the kernel does not use, sized so that a CU holds 16 of its
+// waves (4 per SIMD) instead of 32: n workgroups of w waves fit where n * bytes <= 160 KiB <
+// (n + 1) * bytes.  The HBM stream then has 4096 concurrent streams (one per resident wave) of
+// two groups in flight each instead of 8192 of one: 92.5-93.4 against 94.2-94.4 us for the
+// 622 MB at T = 1024, V = 151936 (same-process A/B, bits equal; a plain read probe of the two
+// patterns: 90.2 against 92.0 us).
+template <typename E, int CPS>
+constexpr unsigned rows_resident_lds() {
+  if constexpr (sizeof(E) != 4) {
+    return 0;
+  } else {
+    constexpr unsigned wgs_per_cu = 16 / waves_for<E>(CPS);
+    return 160u * 1024u / (wgs_per_cu + 1) + 1;
+  }
+}
+
 template <typename E, int CPS>
 hipError_t launch_rows_t(const E* X, const LogitsArgs& a, hipStream_t stream) {
   const dim3 grid = split_grid(a.T, (unsigned)(8 / CPS));
   const dim3 block(64 * waves_for<E>(CPS));
+  const unsigned lds = rows_resident_lds<E, CPS>();
   if (a.vec)
-    hipLaunchKernelGGL((row_reduce_kernel<E, CPS, true>), grid, block, 0, stream, X, a.ld, a.T,
+    hipLaunchKernelGGL((row_reduce_kernel<E, CPS, true>), grid, block, lds, stream, X, a.ld, a.T,
                        a.V, a.Vc, a.targets, a.c, a.beta, a.lp, a.ent, a.ws, a.root);
   else
     hipLaunchKernelGGL((row_reduce_kernel<E, CPS, false>), grid, block, 0, stream, X, a.ld, a.T,
