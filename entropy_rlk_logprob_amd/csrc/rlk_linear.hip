@@ -27,6 +27,9 @@
 
 #include <type_traits>
 
+#include <algorithm>
+#include <atomic>
+
 #include "rlk_launch.hpp"
 #include "rlk_mma_tile.hpp"
 #include "rlk_state.hpp"
@@ -95,125 +98,201 @@ __device__ __forceinline__ State leaf64(const float (&v)[4][16], float c) {
   return r;
 }
 
-// G: token tiles per group of the tile order (see grouped_tile_of and launch_linear_path).
+// G: token tiles per group of the tile order (see grouped_tile_at and launch_linear_path).
+// Persistent: the grid is a multiple of 8 workgroups, at most one per compute unit, and
+// workgroup b takes the tile-order ids b, b + gridDim.x, b + 2 gridDim.x, ... (the same XCD,
+// b mod 8, for all of them).  Right after a tile's K loop the workgroup issues the next
+// tile's first stage and targets, which land while this tile's epilogue runs; the epilogue
+// waits for no global load.  Every tile's arithmetic, and so every bit, is that of a
+// workgroup that takes the tile alone.
 template <bool WITH_U, int G = 8>
 __global__ __launch_bounds__(kThreads, 1) void linear_tile_kernel(
     const uint16_t* __restrict__ H, int64_t ldh, const uint16_t* __restrict__ W, int64_t ldw,
     int64_t d, TileGeom g, const int64_t* __restrict__ targets, float c,
     WireState* __restrict__ tile_states, float* __restrict__ target_logit) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+  // Two K-loop stages, then the targets of a tile's 256 tokens in two buffers (tile parity),
+  // staged by LDS-DMA with the tile's first stage so that the epilogue reads them from LDS
+  // and waits for no load.  One LDS array for every LDS-DMA destination: with a second one
+  // the compiler cannot tell a stage load from a fragment read and waits for every load in
+  // flight before the fragment reads that follow the stage loads.
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes + 2 * kTileT * 8];
+  int64_t (*tgt_lds)[kTileT] = reinterpret_cast<int64_t (*)[kTileT]>(smem + 2 * kStageBytes);
 
-  // Vocabulary tiles x token tiles, token tiles in groups of G (see grouped_tile_of).
-  int64_t vt, tt;
-  if (!mma::grouped_tile_of<G>(g.n_vt, g.n_tt, vt, tt)) return;
-  const int64_t chunk = vt / g.tpc;
-  const int64_t kin = vt % g.tpc;
-  const int64_t chunk_lo = min(chunk * g.Vc, g.V);
-  const int64_t chunk_hi = min(chunk_lo + g.Vc, g.V);
-  const int64_t v_lo = chunk_lo + kin * kTileV;
-  const int64_t v_hi = min(v_lo + (int64_t)kTileV, chunk_hi);
-  const int64_t t_lo = tt * kTileT;
-  if (v_lo >= v_hi) {
-    // Empty tile (short chunk): identity states so that the tile tree sees no data.
-    for (int j = threadIdx.x; j < kTileT; j += kThreads) {
-      const int64_t tok = t_lo + j;
-      if (tok < g.T) tile_states[vt * g.T + tok] = to_wire(identity_state(), 0.0f);
-    }
-    return;
-  }
-
-  const int n_valid = (int)(v_hi - v_lo);
+  const int64_t nb = g.n_vt * g.n_tt;
+  const int64_t n_ids = 8 * ((nb + 7) / 8);
+  const int64_t stride = gridDim.x;
+  const int nk = (int)(d / kBK);
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int wave = wave_id();
   const int wv = wave >> 2;  // vocab half (0, 1)
   const int wt = wave & 3;   // token quarter (0..3)
 
-  floatx16 acc[4][2];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
-  const int w_last = (int)min(g.V - 1 - v_lo, (int64_t)(kTileV - 1));
-  const int h_last = (int)min(g.T - 1 - t_lo, (int64_t)(kTileT - 1));
-  mma::mma_tile(W + v_lo * ldw, ldw, w_last, H + t_lo * ldh, ldh, h_last, 0, (int)(d / kBK), smem,
-                acc);
-  __syncthreads();
-  const int frow = lane & 31;
-  const int fhalf = lane >> 5;
+  // 32-bit tile coordinates (V < 2^26, T < 2^31): the tile loop keeps them in scalar
+  // registers across the K loop, which needs nearly all of them.
+  struct TileRef {
+    int vt, v_lo, v_hi, t_lo;
+  };
+  const int T32 = (int)g.T, V32 = (int)g.V, Vc32 = (int)g.Vc, tpc32 = (int)g.tpc;
+  // The next tile with vocabulary rows at or after id `id` of the tile order; empty tiles
+  // (short chunks) met on the way get identity states, so that the tile tree sees no data.
+  auto next_tile = [&](int64_t& id, TileRef& r) -> bool {
+    for (; id < n_ids; id += stride) {
+      int64_t vt, tt;
+      if (!mma::grouped_tile_at<G>(id, g.n_vt, g.n_tt, vt, tt)) continue;
+      const int vt32 = (int)vt;
+      const int chunk = vt32 / tpc32;
+      const int kin = vt32 - chunk * tpc32;
+      const int chunk_lo = min(chunk * Vc32, V32);
+      const int chunk_hi = min(chunk_lo + Vc32, V32);
+      const int v_lo = chunk_lo + kin * kTileV;
+      const int v_hi = min(v_lo + kTileV, chunk_hi);
+      const int t_lo = (int)tt * kTileT;
+      if (v_lo >= v_hi) {
+        for (int j = tid; j < kTileT; j += kThreads) {
+          const int tok = t_lo + j;
+          if (tok < T32) tile_states[(int64_t)vt32 * T32 + tok] = to_wire(identity_state(), 0.0f);
+        }
+        continue;
+      }
+      r = TileRef{vt32, v_lo, v_hi, t_lo};
+      id += stride;
+      return true;
+    }
+    return false;
+  };
+  auto operand_w = [&](const TileRef& r) {
+    return mma::Operand{W + (int64_t)r.v_lo * ldw, ldw, min(V32 - 1 - r.v_lo, kTileV - 1), 0};
+  };
+  auto operand_h = [&](const TileRef& r) {
+    return mma::Operand{H + (int64_t)r.t_lo * ldh, ldh, min(T32 - 1 - r.t_lo, kTileT - 1), 0};
+  };
 
-  // ---------------------------------------------------------------- epilogue
-  // Each lane owns tokens wt*64 + b*32 + (lane%32), b = 0, 1, and for each of them the
-  // 64 vocab rows wv*128 + a*32 + 8*(i/4) + 4*(lane/32) + (i%4).
-  State half_state[2];
-  // Two instantiations: only the last tile of a chunk has rows at or beyond n_valid to mask,
-  // and keeping that test out of the common one keeps its selects and copies out too.
-  auto token_epilogue = [&](auto masked) {
+  // One dword per lane: wave w stages bytes 256 w .. 256 w + 255 of the tile's 2 KiB of
+  // targets (tokens at or beyond T read token T - 1's and are never used).
+  auto issue_targets = [&](int t_lo, int buf) {
+    if (!targets) return;
+    const int dw = wave * 64 + mma::lane_id_here();
+    const int tok = min(t_lo + (dw >> 1), T32 - 1);
+    const char* src = reinterpret_cast<const char*>(targets + tok) + 4 * (dw & 1);
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)src,
+        (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(tgt_lds[buf]) +
+                                                  wave * 256),
+        4, 0, 0);
+  };
+
+  int64_t id = blockIdx.x;
+  TileRef cur;
+  if (!next_tile(id, cur)) return;
+  int p = 0;   // buffer of the current tile's first stage
+  int tb = 0;  // buffer of the current tile's targets
+  bool issued = false;
+  issue_targets(cur.t_lo, tb);
+  while (true) {
+    TileRef nxt;
+    const bool has_next = next_tile(id, nxt);
+    const mma::Operand A = operand_w(cur), B = operand_h(cur);
+    floatx16 acc[4][2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int tok_in_tile = wt * 64 + b * 32 + frow;
-      const int64_t tok = t_lo + tok_in_tile;
-      const int64_t tgt = (tok < g.T && targets) ? targets[tok] : -1;
-      // Target row relative to this tile (-1 when the target is not in the tile), and
-      // relative to this wave's vocab half.  Row r of the half is held by the lanes with
-      // fhalf = (r / 4) % 2, in register i = 4 ((r / 8) % 4) + r % 4 of block a = r / 32.
-      const int tloc = (tgt >= v_lo && tgt < v_hi) ? (int)(tgt - v_lo) : -1;
-      const int r = tloc - wv * 128;
-      const bool mine = tloc >= 0 && (unsigned)r < 128u && ((r >> 2) & 1) == fhalf;
-      // Only about one token in twenty per wave has its target in this wave's rows, so
-      // the capture sits behind a branch that whole waves skip.
-      if (mine) {
-        const int idx = ((r >> 5) << 4) | (((r >> 3) & 3) << 2) | (r & 3);  // 16 a + i
-        float xt = 0.0f;
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+    mma::mma_tile_op<false, false, 2, true>(A, B, 0, nk, smem, acc, p, issued);
+    // The next tile's first stage and targets, landing while this tile's epilogue runs.
+    if (has_next) {
+      mma::issue_first_stage(operand_w(nxt), operand_h(nxt), smem, (p + nk) & 1);
+      issue_targets(nxt.t_lo, tb ^ 1);
+    }
+    // Every wave is done reading this tile's stages; the next tile's first stage may still
+    // be landing in the other buffer, so the barrier waits for LDS work only.
+    mma::lds_barrier();
+
+    // -------------------------------------------------------------- epilogue
+    // Each lane owns tokens wt*64 + b*32 + (lane%32), b = 0, 1, and for each of them the
+    // 64 vocab rows wv*128 + a*32 + 8*(i/4) + 4*(lane/32) + (i%4).
+    const int elane = mma::lane_id_here();
+    const int frow = elane & 31;
+    const int fhalf = elane >> 5;
+    const int t_lo = cur.t_lo, v_lo = cur.v_lo, v_hi = cur.v_hi;
+    const int n_valid = v_hi - v_lo;
+    State half_state[2];
+    // Two instantiations: only the last tile of a chunk has rows at or beyond n_valid to
+    // mask, and keeping that test out of the common one keeps its selects and copies out too.
+    auto token_epilogue = [&](auto masked) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int tok = t_lo + wt * 64 + b * 32 + frow;
+        // A target outside [0, V) is in no tile.
+        const int64_t t64 = (tok < T32 && targets) ? tgt_lds[tb][wt * 64 + b * 32 + frow] : -1;
+        const int tg = (t64 >= 0 && t64 < V32) ? (int)t64 : -1;
+        // Target row relative to this tile (-1 when the target is not in the tile), and
+        // relative to this wave's vocab half.  Row r of the half is held by the lanes with
+        // fhalf = (r / 4) % 2, in register i = 4 ((r / 8) % 4) + r % 4 of block a = r / 32.
+        const int tloc = (tg >= v_lo && tg < v_hi) ? tg - v_lo : -1;
+        const int r = tloc - wv * 128;
+        const bool mine = tloc >= 0 && (unsigned)r < 128u && ((r >> 2) & 1) == fhalf;
+        // Only about one token in twenty per wave has its target in this wave's rows, so
+        // the capture sits behind a branch that whole waves skip.
+        if (mine) {
+          const int idx = ((r >> 5) << 4) | (((r >> 3) & 3) << 2) | (r & 3);  // 16 a + i
+          float xt = 0.0f;
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xt = (idx == 16 * a + i) ? acc[a][b][i] : xt;
+          target_logit[tok] = xt;
+        }
+
+        float v[4][16];
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) xt = (idx == 16 * a + i) ? acc[a][b][i] : xt;
-        target_logit[tok] = xt;
-      }
-
-      float v[4][16];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          v[a][i] = acc[a][b][i];
-          if constexpr (decltype(masked)::value) {
-            const int vr = wv * 128 + a * 32 + 8 * (i >> 2) + 4 * fhalf + (i & 3);
-            v[a][i] = (vr < n_valid) ? v[a][i] : kNegInf;
+          for (int i = 0; i < 16; ++i) {
+            v[a][i] = acc[a][b][i];
+            if constexpr (decltype(masked)::value) {
+              const int vr = wv * 128 + a * 32 + 8 * (i >> 2) + 4 * fhalf + (i & 3);
+              v[a][i] = (vr < n_valid) ? v[a][i] : kNegInf;
+            }
           }
-        }
-      const State st = leaf64<WITH_U>(v, c);
-      const State o = shfl_xor_state(st, 32);
-      half_state[b] = fhalf ? rlk_merge(o, st, c) : rlk_merge(st, o, c);
-    }
-  };
-  if (n_valid < kTileV)
-    token_epilogue(std::true_type{});
-  else
-    token_epilogue(std::false_type{});
+        const State st = leaf64<WITH_U>(v, c);
+        const State o = shfl_xor_state(st, 32);
+        half_state[b] = fhalf ? rlk_merge(o, st, c) : rlk_merge(st, o, c);
+      }
+    };
+    if (n_valid < kTileV)
+      token_epilogue(std::true_type{});
+    else
+      token_epilogue(std::false_type{});
 
-  // Cross-half merge through LDS: the upper vocab half (wv = 1) publishes its states,
-  // the lower half merges (lower range first) and stores the tile state.
-  State* xch = reinterpret_cast<State*>(smem);
-  if (wv == 1 && fhalf == 0) {
+    // Cross-half merge through LDS, in the buffer of this tile's last stage (the next tile's
+    // first stage goes to the other one): the upper vocab half (wv = 1) publishes its
+    // states, the lower half merges (lower range first) and stores the tile state.
+    State* xch = reinterpret_cast<State*>(smem + ((p + nk - 1) & 1) * kStageBytes);
+    if (wv == 1 && fhalf == 0) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) xch[wt * 64 + b * 32 + frow] = half_state[b];
-  }
-  __syncthreads();
-  if (wv == 0 && fhalf == 0) {
+      for (int b = 0; b < 2; ++b) xch[wt * 64 + b * 32 + frow] = half_state[b];
+    }
+    mma::lds_barrier();
+    if (wv == 0 && fhalf == 0) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int tok_in_tile = wt * 64 + b * 32 + frow;
-      const int64_t tok = t_lo + tok_in_tile;
-      if (tok < g.T) {
-        const State r = rlk_merge(half_state[b], xch[tok_in_tile], c);
-        tile_states[vt * g.T + tok] = to_wire(r, 0.0f);
+      for (int b = 0; b < 2; ++b) {
+        const int tok_in_tile = wt * 64 + b * 32 + frow;
+        const int tok = t_lo + tok_in_tile;
+        if (tok < T32) {
+          const State r = rlk_merge(half_state[b], xch[tok_in_tile], c);
+          tile_states[(int64_t)cur.vt * T32 + tok] = to_wire(r, 0.0f);
+        }
       }
     }
+    if (!has_next) break;
+    cur = nxt;
+    p = (p + nk) & 1;
+    tb ^= 1;
+    issued = true;
   }
+  mma::wait_dma();  // every stage load of this workgroup has landed before it ends
 }
 
 // Batches of at most 128 tokens: one workgroup takes a pair of consecutive vocabulary tiles
@@ -485,6 +564,26 @@ LinearWorkspace linear_workspace_layout(int64_t T, int64_t V, int S) {
   return L;
 }
 
+// Compute units of the current device rounded down to a multiple of 8 (the XCD count), so
+// that a persistent workgroup b stays on XCD b mod 8 for every tile it takes.  Cached per
+// device.
+static int64_t persistent_workgroups() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cached[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cu < 8)
+      cu = 256;
+    n = cu / 8 * 8;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream) {
   const LinearWorkspace L = linear_workspace_layout(a.T, a.V, a.S);
   TileGeom g;
@@ -523,8 +622,10 @@ hipError_t launch_linear_path(const LinearArgs& a, hipStream_t stream) {
     // every 8 vocabulary tiles, W read by two XCDs) measured +0.2 to +0.5 points at T = 2048
     // over one group of 8 (three same-process A/Bs on three boxes, bits equal); with up to 4 token tiles both give
     // one group, and with more than 8, groups of 8 (T = 16384: 51.9% against 51.0% with 4).
+    // Persistent: at most one workgroup per compute unit, a multiple of 8 of them.
+    const int64_t grid = std::min<int64_t>(nb_pad, persistent_workgroups());
     auto launch = [&](auto kernel) {
-      hipLaunchKernelGGL(kernel, split_grid(nb_pad), dim3(kThreads), 0, stream, a.H, a.ldh, a.W,
+      hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a.H, a.ldh, a.W,
                          a.ldw, a.d, g, a.targets, a.c,
                          reinterpret_cast<WireState*>(base + L.tile_states),
                          reinterpret_cast<float*>(base + L.target_logit));

@@ -19,7 +19,8 @@
 // columns so that ds_read_b128 of 16 consecutive rows hits distinct banks; a K-major slab
 // holds 512-byte rows (one k, 256 tile rows) swizzled so that the four k rows one
 // transpose load touches fall in four different bank groups.  Global -> LDS by direct
-// LDS-DMA loads (global_load_lds_dwordx4), issued one stage ahead.
+// LDS-DMA loads (global_load_lds_dwordx4; buffer_load_dwordx4 ... lds in the chained form
+// of persistent kernels), issued one stage ahead.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -55,10 +56,35 @@ constexpr int kSchedVmemRead = 0x020;
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// The lane id from an opaque instruction pair: per-lane values derived from it are formed
+// where they are used.  In a persistent kernel's tile loop, values derived from threadIdx
+// alone would be hoisted out of the loop and held across the K loop in registers it needs.
+__device__ __forceinline__ int lane_id_here() {
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  return lane;
+}
+
 // Workgroup barrier ordering LDS reads (this wave's ds_reads done, then s_barrier).  The
 // LDS-DMA stage that the next step reads was waited for by every wave before it arrives.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 16 bytes per lane from base + voffset + soffset (bytes) into LDS at dst + 16 lane, by a
+// buffer load to LDS on a raw buffer resource over base (stride 0, 0xffffffff records, so
+// no offset is range-checked away; 32-bit data format).  Its only vector operand is the
+// 32-bit offset register.  The resource type exists in the device pass only.
+__device__ __forceinline__ void buffer_load_lds16(const uint16_t* base, uint32_t voffset,
+                                                  int soffset, char* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, -1, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                           voffset, soffset, 0, 0);
+#else
+  (void)base, (void)voffset, (void)soffset, (void)dst;
+#endif
 }
 
 // LDS slab layout: rows of kBK bf16 = 128 bytes; 16-byte column c16 of row r sits at
@@ -90,9 +116,12 @@ __device__ __forceinline__ v4i16 ds_read_tr16(const char* p) {
 
 // One MFMA operand fragment (rows base .. base + 31 of the slab, k 16 ks .. 16 ks + 15):
 // lane l holds row base + l % 32, k = 16 ks + 8 (l / 32) + j, j = 0..7.
+// lane_in: the caller's lane id (a persistent kernel's, see lane_id_here), or -1 for
+// threadIdx.x % 64.
 template <bool KMAJOR>
-__device__ __forceinline__ bf16x8 read_fragment(const char* slab, int base, int ks) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ bf16x8 read_fragment(const char* slab, int base, int ks,
+                                                int lane_in = -1) {
+  const int lane = lane_in < 0 ? (int)(threadIdx.x & 63) : lane_in;
   if constexpr (!KMAJOR) {
     const int c16 = 2 * ks + (lane >> 5);
     return __builtin_bit_cast(bf16x8,
@@ -142,15 +171,25 @@ struct Operand {
 //   k0, nk  first K element (multiple of 8) and number of 64-wide K steps (>= 1)
 // WA = 4: a 512 x 128 tile instead (waves 4 (A side) x 2 (B side), each still 128 x 64;
 // K-contiguous operands only), with 80 KiB stages: for batches of at most 128 tokens.
-template <bool A_KMAJOR, bool B_KMAJOR, int WA = 2>
+// CHAIN (persistent kernels, WA = 2, K-contiguous operands, k0 = 0): stage 0 sits in buffer
+// p0 -- already issued when `issued` (by issue_first_stage, for instance while the previous
+// tile's epilogue ran), else issued here; the last K step issues no loads, and nothing is
+// waited for at the end, so the caller may issue the next tile's first stage into buffer
+// (p0 + nk) % 2 right away (every wave has passed the barrier after which that buffer is
+// no longer read); the next tile's first K step waits for it.
+template <bool A_KMAJOR, bool B_KMAJOR, int WA = 2, bool CHAIN = false>
 __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, int64_t k0,
-                                            int nk, char* smem, floatx16 (&acc)[4][2]) {
+                                            int nk, char* smem, floatx16 (&acc)[4][2],
+                                            int p0 = 0, bool issued = false) {
+  static_assert(!CHAIN || (WA == 2 && !A_KMAJOR && !B_KMAJOR), "chained tiles: K-contiguous");
   static_assert(WA == 2 || (WA == 4 && !A_KMAJOR && !B_KMAJOR), "512-row tiles: K-contiguous");
   constexpr int kARows = 128 * WA;                   // 256 or 512
   constexpr int kBRows = 64 * (8 / WA);              // 256 or 128
   constexpr int kStage = (kARows + kBRows) * kBK * 2;  // 64 or 80 KiB
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  // CHAIN: the per-lane address math below is formed anew for each tile (lane_id_here).
+  int lane = tid & 63;
+  if constexpr (CHAIN) lane = lane_id_here();
   const int wave = wave_id();
   const int wv = wave / (8 / WA);  // A-side 128-row slice (0, 1; or 0..3)
   const int wt = wave % (8 / WA);  // B-side 64-row slice (0..3; or 0, 1)
@@ -167,6 +206,12 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
   constexpr int kWBlocks = kARows / 8;
   int64_t src_off[kBlocksPerWave];  // K-contiguous: offset at k = 0
   int kmaj_row[kBlocksPerWave];     // K-major: k row within the step
+  // CHAIN: the same K-contiguous offsets in bytes, 32-bit (rows < 256, ld <= 2^22, so below
+  // 2^31), for buffer loads to LDS on one buffer resource per operand: the per-lane offset
+  // register is the load's only vector operand, so there is no 64-bit address temporary
+  // that the register allocator could hand to a fragment read while the load is in flight
+  // (which costs a wait for every load in flight).
+  uint32_t src_off_b[kBlocksPerWave];
 #pragma unroll
   for (int i = 0; i < kBlocksPerWave; ++i) {
     const int blk = i * 8 + wave;
@@ -178,11 +223,13 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
       const int row = bb * 8 + (lane >> 3);
       const int col = ((lane & 7) ^ ((row >> 1) & 7)) * 8;
       src_off[i] = (int64_t)min(row, op.last) * op.ld + col;
+      src_off_b[i] = (uint32_t)(min(row, op.last) * (uint32_t)op.ld + col) * 2u;
       kmaj_row[i] = 0;
     } else {
       const int k = bb * 2 + (lane >> 5);
       const int col = min(((lane & 31) ^ ((k & 3) << 2)) * 8, op.last & ~7);
       src_off[i] = col;
+      src_off_b[i] = 0;
       kmaj_row[i] = k;
     }
   }
@@ -193,14 +240,18 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
       const bool is_a = i < kWBlocks / 8;
       const bool kmaj = is_a ? A_KMAJOR : B_KMAJOR;
       const Operand& op = is_a ? A : B;
-      const uint16_t* src;
-      if (!kmaj)
-        src = op.p + k + src_off[i];
-      else
-        src = op.p + min(k + kmaj_row[i], op.k_last) * op.ld + src_off[i];
       char* dst = smem + stage * kStage + blk * 1024;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      if constexpr (CHAIN) {
+        buffer_load_lds16(is_a ? A.p : B.p, src_off_b[i], (int)(k * 2), dst);
+      } else {
+        const void* src;
+        if (!kmaj)
+          src = op.p + k + src_off[i];
+        else
+          src = op.p + min(k + kmaj_row[i], op.k_last) * op.ld + src_off[i];
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      }
     }
   };
   // LDS reads per MFMA step: four A fragments and two B fragments, two transpose loads
@@ -223,7 +274,7 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
   // eight MFMAs keep the matrix unit busy while the first fragments of K step kt come
   // from LDS, instead of both waves of the SIMD idling through that latency.  Every
   // accumulator still sees its MFMAs in K order.
-  auto k_step = [&](int kt, auto deferred) {
+  auto k_step = [&](int kt, auto deferred, auto last) {
     // Stage kt has landed for every wave, and every wave is done reading stage kt - 1,
     // whose buffer the loads of stage kt + 1 now overwrite.  A wave waits at normal issue
     // priority and runs its MFMA steps at raised priority, so that the SIMD's arbiter
@@ -231,21 +282,23 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
     __builtin_amdgcn_s_setprio(0);
     wait_dma();
     lds_barrier();
-    const char* wb = smem + (kt & 1) * kStage;
+    const char* wb = smem + ((kt + p0) & 1) * kStage;
     const char* hb = wb + kARows * kBK * 2;
     auto read_frags = [&](int ks, int buf) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) af[buf][a] = read_fragment<A_KMAJOR>(wb, wv * 128 + a * 32, ks);
+      for (int a = 0; a < 4; ++a) af[buf][a] = read_fragment<A_KMAJOR>(wb, wv * 128 + a * 32, ks, CHAIN ? lane : -1);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) bfr[buf][b] = read_fragment<B_KMAJOR>(hb, wt * 64 + b * 32, ks);
+      for (int b = 0; b < 2; ++b) bfr[buf][b] = read_fragment<B_KMAJOR>(hb, wt * 64 + b * 32, ks, CHAIN ? lane : -1);
     };
     read_frags(0, 0);
     __builtin_amdgcn_s_setprio(1);
     sched_group(kSchedDsRead, kReads);
     // Loads of stage kt + 1 into the other buffer.  Issued on every stage (the last one
-    // repeats stage nk - 1 into the idle buffer) so that they stay in this scheduling
-    // region and can be spread between MFMAs instead of stalling the wave.
-    issue_stage(k0 + (int64_t)min(kt + 1, nk - 1) * kBK, (kt + 1) & 1);
+    // repeats stage nk - 1 into the idle buffer; chained: the last one issues none) so that
+    // they stay in this scheduling region and can be spread between MFMAs instead of
+    // stalling the wave.
+    if constexpr (!decltype(last)::value)
+      issue_stage(k0 + (int64_t)min(kt + 1, nk - 1) * kBK, (kt + 1 + p0) & 1);
     // Instruction order (left to itself the scheduler merges the two fragment buffers,
     // waits on each read right away and issues all stage loads in one burst ahead of the
     // MFMAs): the deferred MFMAs interleaved with the eight stage loads; then MFMA steps
@@ -269,12 +322,46 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
     }
   };
 
-  issue_stage(k0, 0);
-  k_step(0, std::false_type{});
-  for (int kt = 1; kt < nk; ++kt) k_step(kt, std::true_type{});
-  mfma_step(1);  // the last K step's deferred MFMA step
-  __builtin_amdgcn_s_setprio(0);
-  wait_dma();  // the repeated last-stage loads land before the caller reuses the LDS
+  if constexpr (CHAIN) {
+    if (!issued) issue_stage(k0, p0);
+    if (nk == 1) {
+      k_step(0, std::false_type{}, std::true_type{});
+    } else {
+      k_step(0, std::false_type{}, std::false_type{});
+      for (int kt = 1; kt < nk - 1; ++kt) k_step(kt, std::true_type{}, std::false_type{});
+      k_step(nk - 1, std::true_type{}, std::true_type{});
+    }
+    mfma_step(1);  // the last K step's deferred MFMA step
+    __builtin_amdgcn_s_setprio(0);
+  } else {
+    issue_stage(k0, 0);
+    k_step(0, std::false_type{}, std::false_type{});
+    for (int kt = 1; kt < nk; ++kt) k_step(kt, std::true_type{}, std::false_type{});
+    mfma_step(1);  // the last K step's deferred MFMA step
+    __builtin_amdgcn_s_setprio(0);
+    wait_dma();  // the repeated last-stage loads land before the caller reuses the LDS
+  }
+}
+
+// The first stage (K offset 0) of a 256 x 256 tile with K-contiguous operands into LDS
+// buffer `stage`, in mma_tile_op's layout (each wave its eight 1 KiB blocks): for a
+// persistent kernel to issue the next tile's first stage ahead of that tile's K loop.
+__device__ __forceinline__ void issue_first_stage(const Operand& A, const Operand& B,
+                                                  char* smem, int stage) {
+  const int lane = lane_id_here();
+  const int wave = wave_id();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int blk = i * 8 + wave;
+    const bool is_a = i < 4;
+    const Operand& op = is_a ? A : B;
+    const int row = (is_a ? blk : blk - 32) * 8 + (lane >> 3);
+    const int col = ((lane & 7) ^ ((row >> 1) & 7)) * 8;
+    const uint16_t* src = op.p + (int64_t)min(row, op.last) * op.ld + col;
+    char* dst = smem + stage * kStageBytes + blk * 1024;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  }
 }
 
 // Workgroup id -> (row tile, column tile) of an n_rt x n_ct grid of output tiles, launched
@@ -283,13 +370,13 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
 // tiles run one group of up to G column tiles at a time, row-tile-major within the group,
 // so that the ~32 tiles an XCD runs at once are a few row tiles times one column group and
 // share both operands' slices in that XCD's L2.  Returns false for the padding ids beyond
-// the grid.
+// the grid.  grouped_tile_at takes the id explicitly (persistent kernels walk the ids b,
+// b + gridDim.x, ... with gridDim.x a multiple of 8, so that id mod 8 stays b's XCD).
 template <int G>
-__device__ __forceinline__ bool grouped_tile_of(int64_t n_rt, int64_t n_ct, int64_t& rt,
-                                                int64_t& ct) {
+__device__ __forceinline__ bool grouped_tile_at(int64_t hw, int64_t n_rt, int64_t n_ct,
+                                                int64_t& rt, int64_t& ct) {
   const int64_t nb = n_rt * n_ct;
   const int64_t per_xcd = (nb + 7) / 8;
-  const int64_t hw = linear_block();
   if (hw >= 8 * per_xcd) return false;
   const int64_t logical = (hw % 8) * per_xcd + hw / 8;
   if (logical >= nb) return false;
@@ -299,6 +386,11 @@ __device__ __forceinline__ bool grouped_tile_of(int64_t n_rt, int64_t n_ct, int6
   rt = idx / gsz;
   ct = grp * G + idx % gsz;
   return true;
+}
+template <int G>
+__device__ __forceinline__ bool grouped_tile_of(int64_t n_rt, int64_t n_ct, int64_t& rt,
+                                                int64_t& ct) {
+  return grouped_tile_at<G>(linear_block(), n_rt, n_ct, rt, ct);
 }
 
 // Both operands K-contiguous.
