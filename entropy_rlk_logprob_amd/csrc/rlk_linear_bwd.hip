@@ -148,7 +148,8 @@ __global__ __launch_bounds__(kThreads, 1) void dx_tile_kernel(
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
-  mma::mma_tile(W + v_lo * ldw, ldw, n_v - 1, H + t_lo * ldh, ldh, n_t - 1, 0, (int)(d / kBK),
+  // Row strides of W and H are at most 2^22 (the ABI's limit): buffer loads to LDS.
+  mma::mma_tile_buf(W + v_lo * ldw, ldw, n_v - 1, H + t_lo * ldh, ldh, n_t - 1, 0, (int)(d / kBK),
                 smem, acc);
 
   const int lane = threadIdx.x & 63;
@@ -366,7 +367,8 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, in
 // 2 x 8, so that each XCD no longer reads the whole token range of dX: 6.994-6.998 ms against
 // 7.005-7.013 ms for the whole backward at T = 2048, d = 4096, V = 151936 (groups of 2:
 // 7.028-7.030 ms).
-template <bool A_KMAJOR, bool B_KMAJOR, bool SHARE_B, bool ACCUM = false>
+// BUF: stages staged by buffer loads to LDS (every row stride at most 2^22; see mma_tile_op).
+template <bool A_KMAJOR, bool B_KMAJOR, bool SHARE_B, bool ACCUM = false, bool BUF = true>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const uint16_t* __restrict__ A, int64_t lda, int64_t M, int64_t a_klast,
     const uint16_t* __restrict__ B, int64_t ldb, int64_t N, int64_t b_klast, int64_t K,
@@ -414,7 +416,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const int b_last = (int)min((int64_t)kTile, N - n_lo) - 1;
     const mma::Operand Aop{A_KMAJOR ? A + m_lo : A + m_lo * lda, lda, a_last, a_klast};
     const mma::Operand Bop{B_KMAJOR ? B + n_lo : B + n_lo * ldb, ldb, b_last, b_klast};
-    mma::mma_tile_op<A_KMAJOR, B_KMAJOR>(Aop, Bop, k_begin, nk, smem, acc);
+    mma::mma_tile_op<A_KMAJOR, B_KMAJOR, 2, false, BUF>(Aop, Bop, k_begin, nk, smem, acc);
   }
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -543,10 +545,18 @@ hipError_t backward_chunk(const LinearArgs& fwd, const LinearBackwardWorkspace& 
     float* part = reinterpret_cast<float*>(base + L.part);
     const int64_t steps = (L.Vp / kBK + kDhSplits - 1) / kDhSplits;
     const int64_t tiles = ((T + kTile - 1) / kTile) * ((d + kTile - 1) / kTile);
-    hipLaunchKernelGGL((gemm_kernel<false, true, true>),
-                       split_grid((tiles + 7) / 8 * 8, kDhSplits), dim3(kThreads), 0,
-                       stream, dx, L.Vp, T, (int64_t)0, a.W, a.ldw, d, V - 1, L.Vp, steps, part,
-                       d, T * d);
+    // Buffer loads to LDS need dX's row stride Vp at most 2^22 (W's is, by the ABI's limit);
+    // larger vocabularies take the global-address loads.  Same bits either way.
+    if (L.Vp <= (int64_t(1) << 22))
+      hipLaunchKernelGGL((gemm_kernel<false, true, true, false, true>),
+                         split_grid((tiles + 7) / 8 * 8, kDhSplits), dim3(kThreads), 0,
+                         stream, dx, L.Vp, T, (int64_t)0, a.W, a.ldw, d, V - 1, L.Vp, steps, part,
+                         d, T * d);
+    else
+      hipLaunchKernelGGL((gemm_kernel<false, true, true, false, false>),
+                         split_grid((tiles + 7) / 8 * 8, kDhSplits), dim3(kThreads), 0,
+                         stream, dx, L.Vp, T, (int64_t)0, a.W, a.ldw, d, V - 1, L.Vp, steps, part,
+                         d, T * d);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t nq = T * (d / 4);
     hipLaunchKernelGGL(splitk_reduce_kernel, split_grid((nq + 255) / 256), dim3(256), 0,

@@ -87,6 +87,19 @@ __device__ __forceinline__ void buffer_load_lds16(const uint16_t* base, uint32_t
 #endif
 }
 
+// Same with a given record count (bytes from base that may be read; lanes beyond read 0).
+__device__ __forceinline__ void buffer_load_lds16_n(const uint16_t* base, uint32_t records,
+                                                    uint32_t voffset, char* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(base), (short)0, (int)records, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                           voffset, 0, 0, 0);
+#else
+  (void)base, (void)records, (void)voffset, (void)dst;
+#endif
+}
+
 // LDS slab layout: rows of kBK bf16 = 128 bytes; 16-byte column c16 of row r sits at
 // physical column c16 ^ ((r / 2) % 8).  The XOR key makes the 16 rows that one 16-lane
 // ds_read_b128 pass touches land in 16 distinct 16-byte bank groups of the 64-bank LDS.
@@ -177,7 +190,10 @@ struct Operand {
 // waited for at the end, so the caller may issue the next tile's first stage into buffer
 // (p0 + nk) % 2 right away (every wave has passed the barrier after which that buffer is
 // no longer read); the next tile's first K step waits for it.
-template <bool A_KMAJOR, bool B_KMAJOR, int WA = 2, bool CHAIN = false>
+// BUF (implied by CHAIN): K-contiguous operands are staged by buffer loads to LDS as in the
+// chained form; the caller guarantees row strides of at most 2^22 elements, so that every
+// per-lane byte offset (255 rows at most) stays below 2^31.
+template <bool A_KMAJOR, bool B_KMAJOR, int WA = 2, bool CHAIN = false, bool BUF = CHAIN>
 __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, int64_t k0,
                                             int nk, char* smem, floatx16 (&acc)[4][2],
                                             int p0 = 0, bool issued = false) {
@@ -229,7 +245,8 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
       const int k = bb * 2 + (lane >> 5);
       const int col = min(((lane & 31) ^ ((k & 3) << 2)) * 8, op.last & ~7);
       src_off[i] = col;
-      src_off_b[i] = 0;
+      // BUF: the byte offset within the stage's k rows (k < 64, ld <= 2^22: below 2^29).
+      src_off_b[i] = ((uint32_t)k * (uint32_t)op.ld + (uint32_t)col) * 2u;
       kmaj_row[i] = k;
     }
   }
@@ -241,8 +258,16 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
       const bool kmaj = is_a ? A_KMAJOR : B_KMAJOR;
       const Operand& op = is_a ? A : B;
       char* dst = smem + stage * kStage + blk * 1024;
-      if constexpr (CHAIN) {
+      if (BUF && !kmaj) {
         buffer_load_lds16(is_a ? A.p : B.p, src_off_b[i], (int)(k * 2), dst);
+      } else if (BUF && kmaj) {
+        // The stage's k rows from k on: a resource based at row k whose records end after
+        // row k_last, so that rows beyond it read as zeros (the other operand holds zeros
+        // there).
+        const int64_t rows = op.k_last - k + 1;
+        const int64_t bytes = rows > 0 ? rows * op.ld * 2 : 0;
+        buffer_load_lds16_n(op.p + k * op.ld, bytes < 0xffffffffll ? (uint32_t)bytes : 0xffffffffu,
+                            src_off_b[i], dst);
       } else {
         const void* src;
         if (!kmaj)
@@ -261,14 +286,20 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
   // Fragments of MFMA step ks live in buffer ks % 2; the fragments of step ks + 1 are read
   // from LDS while the MFMAs of step ks run.
   bf16x8 af[2][4], bfr[2][2];
-  auto mfma_step = [&](int buf) {
+  auto mfma_ab = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[2]) {
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int b = 0; b < 2; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][a], bfr[buf][b], acc[a][b],
-                                                            0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
   };
+  auto mfma_step = [&](int buf) { mfma_ab(af[buf], bfr[buf]); };
+  // A K-major B operand (and a K-contiguous A): all of a K step's B fragments are read right
+  // after the barrier, before the step's stage loads are issued.  The compiler waits for
+  // every LDS-DMA load in flight before a transpose load that follows one (it does not for
+  // ds_read_b128), which with the transpose loads spread over the MFMA steps put a wait for
+  // the next stage's loads in the middle of every K step.
+  constexpr bool kBEarly = B_KMAJOR && !A_KMAJOR && WA == 2;
   // One K step.  The last MFMA step of K step kt - 1 (DEFERRED) is held back until after
   // the barrier that opens K step kt: its fragments are already in registers, so its
   // eight MFMAs keep the matrix unit busy while the first fragments of K step kt come
@@ -290,9 +321,21 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
 #pragma unroll
       for (int b = 0; b < 2; ++b) bfr[buf][b] = read_fragment<B_KMAJOR>(hb, wt * 64 + b * 32, ks, CHAIN ? lane : -1);
     };
-    read_frags(0, 0);
-    __builtin_amdgcn_s_setprio(1);
-    sched_group(kSchedDsRead, kReads);
+    bf16x8 bk[4][2];  // kBEarly: this K step's B fragments
+    if constexpr (kBEarly) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) af[0][a] = read_fragment<false>(wb, wv * 128 + a * 32, 0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) bk[ks][b] = read_fragment<true>(hb, wt * 64 + b * 32, ks);
+      __builtin_amdgcn_s_setprio(1);
+      sched_group(kSchedDsRead, 4 + 16);
+    } else {
+      read_frags(0, 0);
+      __builtin_amdgcn_s_setprio(1);
+      sched_group(kSchedDsRead, kReads);
+    }
     // Loads of stage kt + 1 into the other buffer.  Issued on every stage (the last one
     // repeats stage nk - 1 into the idle buffer; chained: the last one issues none) so that
     // they stay in this scheduling region and can be spread between MFMAs instead of
@@ -313,12 +356,27 @@ __device__ __forceinline__ void mma_tile_op(const Operand& A, const Operand& B, 
     } else {
       sched_group(kSchedVmemRead, kBlocksPerWave);
     }
+    if constexpr (kBEarly) {
 #pragma unroll
-    for (int ks = 0; ks < 3; ++ks) {
-      read_frags(ks + 1, (ks + 1) & 1);
-      mfma_step(ks & 1);
-      sched_reads_over_mfmas<kReads, 0>();
-      sched_group(kSchedMfma, 2);
+      for (int ks = 0; ks < 3; ++ks) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          af[(ks + 1) & 1][a] = read_fragment<false>(wb, wv * 128 + a * 32, ks + 1);
+        mfma_ab(af[ks & 1], bk[ks]);
+        sched_reads_over_mfmas<4, 0>();
+        sched_group(kSchedMfma, 2);
+      }
+      // MFMA step 3 is held back (it runs as the next K step's deferred step).
+#pragma unroll
+      for (int b = 0; b < 2; ++b) bfr[1][b] = bk[3][b];
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 3; ++ks) {
+        read_frags(ks + 1, (ks + 1) & 1);
+        mfma_step(ks & 1);
+        sched_reads_over_mfmas<kReads, 0>();
+        sched_group(kSchedMfma, 2);
+      }
     }
   };
 
@@ -403,6 +461,14 @@ __device__ __forceinline__ void mma_tile(const uint16_t* __restrict__ At, int64_
                                          floatx16 (&acc)[4][2]) {
   mma_tile_op<false, false>(Operand{At, lda, a_last, 0}, Operand{Bt, ldb, b_last, 0}, k0, nk,
                             smem, acc);
+}
+// Same, staged by buffer loads to LDS (row strides of at most 2^22 elements).
+__device__ __forceinline__ void mma_tile_buf(const uint16_t* __restrict__ At, int64_t lda,
+                                             int a_last, const uint16_t* __restrict__ Bt,
+                                             int64_t ldb, int b_last, int64_t k0, int nk,
+                                             char* smem, floatx16 (&acc)[4][2]) {
+  mma_tile_op<false, false, 2, false, true>(Operand{At, lda, a_last, 0},
+                                            Operand{Bt, ldb, b_last, 0}, k0, nk, smem, acc);
 }
 
 }  // namespace mma

@@ -125,6 +125,36 @@ def test_token_tile_groups_with_partial_last_group(lib, T, group):
     assert bitwise_equal(lpt, lp[lo:]) and bitwise_equal(entt, ent[lo:])
 
 
+def test_persistent_walk_over_empty_and_edge_tiles(lib):
+    """The forward kernel runs one workgroup per compute unit, each walking several ids of the
+    tile order and loading the next tile's first stage and targets during the current tile's
+    epilogue.  V = 40965 gives chunks of Vc = 5124 columns: 21 vocabulary tiles per chunk, the
+    21st holding 4 columns, except in the last chunk (5097 columns), where it is empty.  T =
+    1300 gives 6 token tiles, the last one 20 tokens.  That is 1008 tiles, about four per
+    workgroup, so a workgroup's walk passes empty tiles and loads edge tiles ahead.  Every row
+    against the oracle at every vocab split, split invariance, the logprob-only kernel, and the
+    first 300 rows alone give the same bits."""
+    import torch
+    T, d, V = 1300, 256, 40965
+    assert 4 * -(-(-(-V // 8)) // 4) == 5124 and V - 7 * 5124 == 5097
+    announce(f"linear T={T} d={d} V={V} (persistent walk: empty and edge tiles)")
+    case = S.random_fused_case(T, d, V, seed=9400, h_sigma=1.0, w_sigma=3.0 / math.sqrt(d),
+                               temperature=0.7)
+    olp, oent = oracle.linear_logprob_entropy(f32(case.h_bits), f32(case.w_bits), case.targets,
+                                              0.7)
+    h, w, t = bits_dev(case.h_bits), bits_dev(case.w_bits), dev(case.targets)
+    lp, ent = run_linear(lib, h, w, t, 0.7)
+    assert max_abs(lp, olp) <= TOL_LINEAR and max_abs(ent, oent) <= TOL_LINEAR
+    for split in (2, 4, 8):
+        lps, ents = run_linear(lib, h, w, t, 0.7, split)
+        assert bitwise_equal(lps, lp) and bitwise_equal(ents, ent), split
+    lp_only, none = lib.linear_logprob(h, w, t, 0.7, 1, with_entropy=False)
+    torch.cuda.synchronize()
+    assert none is None and bitwise_equal(lp_only.cpu().numpy(), lp)
+    lpa, enta = run_linear(lib, h[:300], w, t[:300], 0.7)
+    assert bitwise_equal(lpa, lp[:300]) and bitwise_equal(enta, ent[:300])
+
+
 def test_uniform_when_weight_is_zero(lib):
     announce("linear zero weight -> uniform")
     T, d, V = 5, 128, 3000

@@ -169,6 +169,31 @@ def test_qwen3_vocab_full_hidden_vs_oracle(lib):
     assert bitwise_equal(dh2, dh) and bitwise_equal(dw2, dw)
 
 
+def test_vocab_past_the_buffer_load_limit_vs_oracle(lib):
+    """V = 2^22 + 100: the logit gradient's padded row stride Vp exceeds 2^22, so dH stages
+    its operands with global-address loads instead of buffer loads to LDS (whose 32-bit
+    per-lane offsets it would overflow).  dH and sampled vocabulary rows of dW against the
+    oracle (the last rows included); vocab split 4 bitwise."""
+    T, d, V = 3, 64, (1 << 22) + 100
+    announce(f"generating linear backward case T={T} d={d} V={V}")
+    case = S.random_fused_case(T, d, V, seed=105, h_sigma=1.0, w_sigma=3.0 / math.sqrt(d))
+    gl, ge = weights(T, 106)
+    hd, wd, td = bits_dev(case.h_bits), bits_dev(case.w_bits), dev(case.targets)
+    gld, ged = dev(gl), dev(ge)
+    announce(f"linear backward T={T} d={d} V={V} (global-address loads for dH)")
+    dh, dw = run_bwd(lib, hd, wd, td, 1.0, 1, gld, ged)
+    h = f32(case.h_bits)
+    w = f32(case.w_bits)
+    gx = oracle.logits_grad(h @ w.T, case.targets, 1.0, gl, ge)
+    check(dh, gx @ w, bound(gx, w, V))
+    vrows = np.unique(np.concatenate([[0, 1, 255, 256, V - 101, V - 2, V - 1],
+                                      np.random.default_rng(107).integers(0, V, 20)]))
+    check(dw[vrows], gx[:, vrows].T @ h, bound(gx[:, vrows].T, h, T))
+    announce(f"linear backward T={T} d={d} V={V} split 4")
+    dh4, dw4 = run_bwd(lib, hd, wd, td, 1.0, 4, gld, ged)
+    assert bitwise_equal(dh4, dh) and bitwise_equal(dw4, dw)
+
+
 def test_saved_row_states_give_the_same_bits(lib):
     import torch
     T, d, V = 200, 128, 9001
