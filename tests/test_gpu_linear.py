@@ -25,6 +25,8 @@ def f32(bits):
 @pytest.mark.parametrize("T,d,V,tau", [
     (1, 64, 1, 1.0), (3, 64, 100, 1.0), (37, 128, 1000, 0.7), (257, 192, 5003, 1.0),
     (300, 256, 20000, 0.7), (513, 64, 2049, 1.0), (64, 512, 151936, 1.0),
+    # more tiles than compute units (640 and 336), so that workgroups walk several tiles
+    (777, 192, 40000, 0.7), (1500, 320, 12345, 1.0),
 ])
 def test_shapes_vs_oracle_and_split_bitwise(lib, T, d, V, tau):
     """Several token and vocab tiles with ragged tails; logits of spread ~3 so that a
