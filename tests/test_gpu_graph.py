@@ -25,6 +25,11 @@ def test_captured_sequence_replays_with_eager_bits(lib):
     ge = dev(rng.normal(size=T).astype(np.float32))
     x, t = dev(lc.x), dev(lc.targets)
     h, w, tf = bits_dev(fc.h_bits), bits_dev(fc.w_bits), dev(fc.targets)
+    # A second fused batch above 128 tokens runs the persistent tile kernel (the batch of 96
+    # runs the paired-tile kernel).
+    T2 = 300
+    fc2 = S.random_fused_case(T2, d, V, seed=123, w_sigma=3.0 / math.sqrt(d))
+    h2, tf2 = bits_dev(fc2.h_bits), dev(fc2.targets)
     mask = torch.ones(T, dtype=torch.uint8, device="cuda")
 
     # every output and workspace exists before capture
@@ -35,13 +40,16 @@ def test_captured_sequence_replays_with_eager_bits(lib):
             flp=torch.empty(T, device="cuda"), fent=torch.empty(T, device="cuda"),
             fst=lib.row_states_buffer(T), dh=torch.empty((T, d), device="cuda"),
             dw=torch.empty((V, d), device="cuda"), cmp=torch.empty(64, dtype=torch.uint8,
-                                                                  device="cuda"))
+                                                                  device="cuda"),
+            flp2=torch.empty(T2, device="cuda"), fent2=torch.empty(T2, device="cuda"))
     ws = {op: torch.empty(max(1, lib.workspace_bytes(op, T, V, dd, 4)), dtype=torch.uint8,
                           device="cuda")
           for op, dd in ((B.OP_FROM_LOGITS, 0), (B.OP_BACKWARD_FROM_LOGITS, 0),
                          (B.OP_LINEAR, d), (B.OP_LINEAR_BACKWARD, d))}
     ws_cmp = torch.empty(max(1, lib.workspace_bytes(B.OP_COMPARE, T, 1)), dtype=torch.uint8,
                          device="cuda")
+    ws2 = torch.empty(lib.workspace_bytes(B.OP_LINEAR, T2, V, d, 1), dtype=torch.uint8,
+                      device="cuda")
 
     def sequence(o):
         lib.logprob_from_logits(x, t, 0.7, 4, out=(o["lp"], o["ent"]),
@@ -54,6 +62,7 @@ def test_captured_sequence_replays_with_eager_bits(lib):
         lib.linear_logprob_backward(h, w, tf, 1.0, 4, gl, ge, out=(o["dh"], o["dw"]),
                                     workspace=ws[B.OP_LINEAR_BACKWARD], row_states=o["fst"])
         lib.logprob_compare_async(o["lp"], o["flp"], mask, out=o["cmp"], workspace=ws_cmp)
+        lib.linear_logprob(h2, w, tf2, 0.7, 1, out=(o["flp2"], o["fent2"]), workspace=ws2)
 
     announce("graph capture: eager reference")
     eager = buffers()
