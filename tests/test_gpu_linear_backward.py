@@ -55,7 +55,7 @@ def weights(T, seed):
 
 @pytest.mark.parametrize("T,d,V,tau", [
     (3, 64, 100, 1.0), (37, 128, 1000, 0.7), (300, 192, 5003, 1.0), (513, 64, 2049, 1.0),
-    (64, 512, 20000, 0.7),
+    (64, 512, 20000, 0.7), (777, 320, 12345, 0.7), (1100, 256, 3001, 1.0),
 ])
 def test_shapes_vs_oracle_and_split_bitwise(lib, T, d, V, tau):
     announce(f"linear backward T={T} d={d} V={V} tau={tau}")
