@@ -41,7 +41,9 @@
  *     all -inf, gives NaN for both outputs of that row; -inf logits are tokens of
  *     probability zero;
  *   - the current HIP device must be a gfx950 GPU, otherwise
- *     RLK_ERR_UNSUPPORTED_DEVICE;
+ *     RLK_ERR_UNSUPPORTED_DEVICE; `stream` and every pointer belong to that device (the
+ *     launch shapes, such as one workgroup per compute unit for the persistent tile
+ *     kernel, are taken from it);
  *   - calls on different streams may run concurrently if they use distinct workspaces.
  */
 #ifndef RLK_LOGPROB_H
